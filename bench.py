@@ -1,0 +1,270 @@
+"""Benchmark of the fused conv / GEMM-logsumexp library on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--cpu-seconds S]
+
+A step is one call of the fused operation (all of its kernels) on one batch of
+synthetic input already resident in HBM. The default workload is the fp32
+conv3x3 + bias + erf-GELU + global average pool on x (64, 16, 224, 224) ->
+(64, 64). Prints ONE JSON line with the whole-job throughput (TFLOP/s of the
+algorithmic contraction), the roofline of the dominant kernel (its average
+launch time from HIP events recorded on the launch stream during the timed
+steps) and a CPU baseline: the fp64 oracle timed on this host on a bounded
+sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import synth  # noqa: E402
+
+PEAK_TFLOPS = {"f32": 157.3, "bf16": 2516.6}  # MI355X dense MFMA peaks
+HBM_GBPS = 8000.0
+DEFAULT_WORKLOAD = "conv_gelu_pool_f32"
+KERNEL_SOURCES = ["gemm_activation_reduction_amd/csrc/conv3x3.hip",
+                  "gemm_activation_reduction_amd/csrc/gemm_lse.hip",
+                  "gemm_activation_reduction_amd/csrc/device_math.h"]
+
+
+def source_hash() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def conv_flops(s) -> float:
+    return 2.0 * s["N"] * s["Cout"] * (s["H"] - 2) * (s["W"] - 2) * s["Cin"] * 9
+
+
+def conv_bytes(s) -> float:
+    esz = 2 if s["dtype"] == "bf16" else 4
+    out = s["N"] * s["Cout"] * (1 if s["pool"] else (s["H"] - 2) * (s["W"] - 2))
+    return esz * (s["N"] * s["Cin"] * s["H"] * s["W"] + s["Cout"] * s["Cin"] * 9) + 4 * s["Cout"] + 4 * out
+
+
+def gemm_flops(s) -> float:
+    return 2.0 * s["M"] * s["K"] * s["N"]
+
+
+def gemm_bytes(s) -> float:
+    return 4.0 * (s["M"] * s["K"] + s["N"] * s["K"] + s["N"] + s["M"])
+
+
+def read_traffic(workload: str, kernel: str):
+    """HBM bytes per launch from the committed rocprofv3 --pmc summary, or None when the
+    summary is missing or the kernel sources changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}.traffic.txt")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    for line in open(path):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            vals[k.strip()] = v.strip()
+    if vals.get("source_hash") != source_hash():
+        return None
+    try:
+        return float(vals["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline_conv(spec, x, w, b, got_pool, seconds):
+    """fp64 oracle on a bounded sample of (n, oc) maps of the same workload."""
+    import oracle
+    N, Cout = spec["N"], spec["Cout"]
+    order = np.random.default_rng(1).permutation(N * Cout)
+    flops_per_map = conv_flops(spec) / (N * Cout)
+    done, t0, errs = 0, time.perf_counter(), []
+    batch = max(1, oracle.num_threads())
+    while done < len(order) and time.perf_counter() - t0 < seconds:
+        sel = order[done:done + batch]
+        n, oc = sel // Cout, sel % Cout
+        ref = oracle.conv_pool_sample(x, w, b, spec["act"], n, oc)
+        if got_pool is not None:
+            errs.append(np.max(np.abs(got_pool[n, oc] - ref) / (1 + np.abs(ref))))
+        done += len(sel)
+    el = time.perf_counter() - t0
+    return {"value": round(done * flops_per_map / el / 1e12, 6), "unit": "TFLOP/s", "cores": oracle.num_threads(),
+            "kind": "oracle", "seconds": round(el, 3),
+            "sample": f"{done} of {N * Cout} (n, oc) output maps ({done * flops_per_map / 1e9:.2f} GFLOP, fp64)",
+            "sample_max_err": float(max(errs)) if errs else None}
+
+
+def cpu_baseline_conv_points(spec, x, w, b, out_dev, seconds):
+    import oracle
+    import torch
+    N, Cout, OH, OW = spec["N"], spec["Cout"], spec["H"] - 2, spec["W"] - 2
+    r = np.random.default_rng(2)
+    flops_per_pt = 2.0 * spec["Cin"] * 9
+    done, t0, errs, batch = 0, time.perf_counter(), [], 200000
+    while time.perf_counter() - t0 < seconds:
+        n, oc = r.integers(0, N, batch), r.integers(0, Cout, batch)
+        oh, ow = r.integers(0, OH, batch), r.integers(0, OW, batch)
+        ref = oracle.conv_point_sample(x, w, b, spec["act"], n, oc, oh, ow)
+        idx = [torch.from_numpy(a.astype(np.int64)).to(out_dev.device) for a in (n, oc, oh, ow)]
+        got = out_dev[idx[0], idx[1], idx[2], idx[3]].cpu().numpy()
+        errs.append(np.max(np.abs(got - ref) / (1 + np.abs(ref))))
+        done += batch
+    el = time.perf_counter() - t0
+    return {"value": round(done * flops_per_pt / el / 1e12, 6), "unit": "TFLOP/s", "cores": oracle.num_threads(),
+            "kind": "oracle", "seconds": round(el, 3),
+            "sample": f"{done} random output points of {N * Cout * OH * OW} ({done * flops_per_pt / 1e9:.2f} GFLOP, fp64)",
+            "sample_max_err": float(max(errs)) if errs else None}
+
+
+def cpu_baseline_gemm(spec, X, W, b, got, seconds):
+    import oracle
+    M = spec["M"]
+    order = np.random.default_rng(3).permutation(M)
+    flops_per_row = gemm_flops(spec) / M
+    done, t0, errs = 0, time.perf_counter(), []
+    batch = max(1, oracle.num_threads())
+    while done < M and time.perf_counter() - t0 < seconds:
+        rows = order[done:done + batch]
+        ref, _ = oracle.gemm_lse_mish(X, W, b, spec["scale"], spec["cmin"], spec["cmax"], rows=rows)
+        errs.append(np.max(np.abs(got[rows] - ref) / (1 + np.abs(ref))))
+        done += len(rows)
+    el = time.perf_counter() - t0
+    return {"value": round(done * flops_per_row / el / 1e12, 6), "unit": "TFLOP/s", "cores": oracle.num_threads(),
+            "kind": "oracle", "seconds": round(el, 3),
+            "sample": f"{done} of {M} rows ({done * flops_per_row / 1e9:.2f} GFLOP, fp64)",
+            "sample_max_err": float(max(errs)) if errs else None}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD,
+                    choices=sorted(list(synth.CONV_WORKLOADS) + list(synth.GEMM_WORKLOADS)))
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="oracle time budget (0: skip)")
+    ap.add_argument("--calib-copy-mb", type=int, default=0,
+                    help="after timing, run plain device copies of this size (HBM counter calibration)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
+              "the multi-GPU sharding is described in DESIGN.md but not launched", file=sys.stderr)
+        return 2
+
+    import torch
+    import gemm_activation_reduction_amd as fc
+
+    dev = torch.device("cuda:0")
+    name = args.workload
+    is_conv = name in synth.CONV_WORKLOADS
+    spec = synth.CONV_WORKLOADS[name] if is_conv else synth.GEMM_WORKLOADS[name]
+    print(f"bench: generating inputs for {name}", file=sys.stderr, flush=True)
+    if is_conv:
+        x, w, b = synth.conv_inputs(spec)
+        bf16 = spec["dtype"] == "bf16"
+        to = (lambda a: torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)) if bf16 else \
+            (lambda a: torch.from_numpy(a).to(dev))
+        xd, wd, bd = to(x), to(w), torch.from_numpy(b).to(dev)
+        act = {0: "none", 1: "gelu", 2: "mish2"}[spec["act"]]
+        out = torch.empty((spec["N"], spec["Cout"]) if spec["pool"] else
+                          (spec["N"], spec["Cout"], spec["H"] - 2, spec["W"] - 2), dtype=torch.float32, device=dev)
+
+        def step():
+            fc.conv_act_pool(xd, wd, bd, act=act, pool=bool(spec["pool"]), out=out)
+        flops, nbytes, kernel, dtype = conv_flops(spec), conv_bytes(spec), "conv3x3_fused", spec["dtype"]
+        cfg = {"workload": name, "x": [spec["N"], spec["Cin"], spec["H"], spec["W"]], "cout": spec["Cout"],
+               "kernel": "3x3 valid stride 1", "act": act, "pool": bool(spec["pool"]), "dtype": dtype}
+    else:
+        X, W, b = synth.gemm_inputs(spec)
+        xd, wd, bd = (torch.from_numpy(a).to(dev) for a in (X, W, b))
+        out = torch.empty((spec["M"], 1), dtype=torch.float32, device=dev)
+
+        def step():
+            fc.gemm_lse_mish(xd, wd, bd, spec["scale"], spec["cmin"], spec["cmax"], out=out)
+        flops, nbytes, kernel, dtype = gemm_flops(spec), gemm_bytes(spec), "gemm_lse_partials", "f32"
+        cfg = {"workload": name, "M": spec["M"], "K": spec["K"], "N": spec["N"], "scale": spec["scale"],
+               "clamp": [spec["cmin"], spec["cmax"]], "dtype": dtype}
+
+    print(f"bench: warmup {args.warmup}, timing {args.steps} steps", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    fc.fconv_profile(True)
+    stream = torch.cuda.current_stream()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    kms, klaunches = fc.fconv_profile_read(kernel)
+    fc.fconv_profile(False)
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    ev_ms_per_step = ev0.elapsed_time(ev1) / args.steps
+    kernel_ms = kms / max(1, klaunches)
+    value = flops / (ms_per_step * 1e-3) / 1e12
+    achieved = flops / (kernel_ms * 1e-3) / 1e12
+    peak = PEAK_TFLOPS[dtype]
+    traffic = read_traffic(name, kernel)
+    print(f"bench: {ms_per_step:.4f} ms/step (events {ev_ms_per_step:.4f}), {kernel} {kernel_ms:.4f} ms/launch "
+          f"over {klaunches} launches, {achieved:.2f} TFLOP/s, {nbytes / (kernel_ms * 1e-3) / 1e9:.1f} GB/s algorithmic",
+          file=sys.stderr, flush=True)
+
+    if args.calib_copy_mb > 0:
+        n = args.calib_copy_mb * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(f"bench: calibration copies of {args.calib_copy_mb} MiB done", file=sys.stderr, flush=True)
+
+    cpu = None
+    if args.cpu_seconds > 0:
+        print(f"bench: CPU oracle baseline (~{args.cpu_seconds:.0f} s)", file=sys.stderr, flush=True)
+        if is_conv and spec["pool"]:
+            cpu = cpu_baseline_conv(spec, x, w, b, out.cpu().numpy(), args.cpu_seconds)
+        elif is_conv:
+            cpu = cpu_baseline_conv_points(spec, x, w, b, out, args.cpu_seconds)
+        else:
+            cpu = cpu_baseline_gemm(spec, X, W, b, out.cpu().numpy()[:, 0], args.cpu_seconds)
+
+    line = {
+        "metric": "fused conv+act+pool TFLOP/s and % MFMA peak; GEMM-LSE TFLOP/s",
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": dtype,
+        "data": "synthetic",
+        "config": cfg,
+        "pct_mfma_peak": round(100.0 * value / peak, 2),
+        "roofline": {"bound": "mfma", "kernel": kernel, "achieved": round(achieved, 3), "peak": peak,
+                     "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": traffic,
+                     "kernel_ms": round(kernel_ms, 5), "algorithmic_bytes": nbytes,
+                     "algorithmic_gbps": round(nbytes / (kernel_ms * 1e-3) / 1e9, 1)},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,229 @@
+// C ABI of the fused conv / GEMM-logsumexp library: argument validation, the
+// per-(device, stream) workspace cache, and dispatch to the kernels.
+#include <cmath>
+#include <cstdint>
+#include <cstdio>
+#include <map>
+#include <mutex>
+#include <string>
+#include <utility>
+#include <vector>
+
+#include "../../include/fconv.h"
+#include "internal.h"
+
+#define FCONV_API extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const std::string& msg) {
+    g_last_error = msg;
+    return code;
+}
+
+int ok() {
+    g_last_error.clear();
+    return FCONV_OK;
+}
+
+constexpr long long kMaxElems = (1LL << 31) - 1;
+
+struct Workspace {
+    void* ptr = nullptr;
+    size_t bytes = 0;
+};
+
+std::mutex g_ws_mutex;
+std::map<std::pair<int, hipStream_t>, Workspace> g_ws;
+
+// Returns a device buffer of at least `bytes` owned by the library for (device, stream).
+// Growth waits for the stream (earlier work may still use the old buffer) before freeing.
+int get_workspace(hipStream_t stream, size_t bytes, void** out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(FCONV_EHIP, std::string("hipGetDevice: ") + hipGetErrorString(e));
+    std::lock_guard<std::mutex> lock(g_ws_mutex);
+    Workspace& ws = g_ws[std::make_pair(dev, stream)];
+    if (ws.bytes < bytes) {
+        if (ws.ptr) {
+            e = hipStreamSynchronize(stream);
+            if (e != hipSuccess)
+                return fail(FCONV_EHIP, std::string("hipStreamSynchronize: ") + hipGetErrorString(e));
+            (void)hipFree(ws.ptr);
+            ws.ptr = nullptr;
+            ws.bytes = 0;
+        }
+        size_t want = bytes < (1u << 20) ? (1u << 20) : bytes;
+        e = hipMalloc(&ws.ptr, want);
+        if (e != hipSuccess) {
+            ws.ptr = nullptr;
+            (void)hipGetLastError();
+            return fail(FCONV_ENOMEM, "workspace hipMalloc(" + std::to_string(want) + "): " + hipGetErrorString(e));
+        }
+        ws.bytes = want;
+    }
+    *out = ws.ptr;
+    return FCONV_OK;
+}
+
+// Per-kernel event timing (fconv_profile / fconv_profile_read).
+struct EventTimer final : fconv::KernelTimer {
+    struct Pending {
+        std::string kernel;
+        hipEvent_t start, stop;
+    };
+    std::mutex mu;
+    bool enabled = false;
+    std::vector<Pending> pending;
+    std::map<std::string, hipEvent_t> open;
+    std::map<std::string, std::pair<double, long long>> totals;  // ms, launches
+
+    void begin(const char* kernel, hipStream_t s) override {
+        hipEvent_t e;
+        if (hipEventCreate(&e) != hipSuccess) return;
+        (void)hipEventRecord(e, s);
+        std::lock_guard<std::mutex> lock(mu);
+        open[kernel] = e;
+    }
+    void end(const char* kernel, hipStream_t s) override {
+        hipEvent_t e;
+        if (hipEventCreate(&e) != hipSuccess) return;
+        (void)hipEventRecord(e, s);
+        std::lock_guard<std::mutex> lock(mu);
+        auto it = open.find(kernel);
+        if (it == open.end()) {
+            (void)hipEventDestroy(e);
+            return;
+        }
+        pending.push_back({kernel, it->second, e});
+        open.erase(it);
+    }
+    // Waits for recorded events and folds them into the totals.
+    int drain() {
+        std::lock_guard<std::mutex> lock(mu);
+        int rc = FCONV_OK;
+        for (auto& p : pending) {
+            float ms = 0.f;
+            if (hipEventSynchronize(p.stop) != hipSuccess || hipEventElapsedTime(&ms, p.start, p.stop) != hipSuccess)
+                rc = FCONV_EHIP;
+            auto& t = totals[p.kernel];
+            t.first += ms;
+            t.second += 1;
+            (void)hipEventDestroy(p.start);
+            (void)hipEventDestroy(p.stop);
+        }
+        pending.clear();
+        return rc;
+    }
+};
+
+EventTimer g_timer;
+
+fconv::KernelTimer* active_timer() { return g_timer.enabled ? &g_timer : nullptr; }
+
+bool overlaps(const void* a, size_t abytes, const void* b, size_t bbytes) {
+    const uintptr_t a0 = (uintptr_t)a, b0 = (uintptr_t)b;
+    return a0 < b0 + bbytes && b0 < a0 + abytes;
+}
+
+}  // namespace
+
+FCONV_API int fconv_version(void) { return 100; }
+
+FCONV_API const char* fconv_last_error(void) { return g_last_error.c_str(); }
+
+FCONV_API int fconv_act_pool(const void* x, const void* w, const float* b, int N, int Cin, int H, int W,
+                             int Cout, int act, int pool, float* out, hipStream_t stream) {
+    if (!x || !w || !b || !out) return fail(FCONV_EINVAL, "fconv_act_pool: null pointer argument");
+    if (N < 1 || Cin < 1 || Cout < 1) return fail(FCONV_EINVAL, "fconv_act_pool: N, Cin and Cout must be >= 1");
+    if (H < 3 || W < 3) return fail(FCONV_EINVAL, "fconv_act_pool: H and W must be >= 3 (3x3 valid conv)");
+    const int kind = act & 0xFF, dt = act & ~0xFF;
+    if (kind != FCONV_ACT_NONE && kind != FCONV_ACT_GELU && kind != FCONV_ACT_MISH2)
+        return fail(FCONV_EINVAL, "fconv_act_pool: unknown activation " + std::to_string(kind));
+    if (dt != FCONV_DT_F32 && dt != FCONV_DT_BF16)
+        return fail(FCONV_EINVAL, "fconv_act_pool: unknown dtype bits in act");
+    if (pool != 0 && pool != 1) return fail(FCONV_EINVAL, "fconv_act_pool: pool must be 0 or 1");
+    const long long nx = (long long)N * Cin * H * W, nw = (long long)Cout * Cin * 9;
+    const long long nout = pool ? (long long)N * Cout : (long long)N * Cout * (H - 2) * (W - 2);
+    if (nx > kMaxElems || nw > kMaxElems || nout > kMaxElems)
+        return fail(FCONV_EINVAL, "fconv_act_pool: a tensor has 2^31 or more elements");
+    const size_t esz = dt == FCONV_DT_BF16 ? 2 : 4;
+    const size_t ob = (size_t)nout * 4;
+    if (overlaps(out, ob, x, nx * esz) || overlaps(out, ob, w, nw * esz) || overlaps(out, ob, b, (size_t)Cout * 4))
+        return fail(FCONV_EINVAL, "fconv_act_pool: out overlaps an input");
+
+    const fconv::ConvPlan plan = fconv::plan_conv(dt == FCONV_DT_BF16, kind, pool, N, Cin, H, W, Cout);
+    if (plan.grid() > 0x7FFFFFFFLL) return fail(FCONV_EUNSUPPORTED, "fconv_act_pool: launch grid too large");
+    void* ws = nullptr;
+    int rc = get_workspace(stream, plan.workspace_bytes(), &ws);
+    if (rc != FCONV_OK) return rc;
+    hipError_t e = fconv::launch_conv(plan, x, w, b, out, ws, stream, active_timer());
+    if (e != hipSuccess) return fail(FCONV_EHIP, std::string("fconv_act_pool launch: ") + hipGetErrorString(e));
+    return ok();
+}
+
+FCONV_API int fgemm_lse_mish(const float* x, const float* w, const float* b, int M, int K, int N, float scale,
+                             float cmin, float cmax, float* out, hipStream_t stream) {
+    if (!x || !w || !b || !out) return fail(FCONV_EINVAL, "fgemm_lse_mish: null pointer argument");
+    if (M < 1 || K < 1 || N < 1) return fail(FCONV_EINVAL, "fgemm_lse_mish: M, K and N must be >= 1");
+    if (!std::isfinite(scale)) return fail(FCONV_EINVAL, "fgemm_lse_mish: scale must be finite");
+    if (std::isnan(cmin) || std::isnan(cmax) || cmin > cmax)
+        return fail(FCONV_EINVAL, "fgemm_lse_mish: need cmin <= cmax (not NaN)");
+    const long long nx = (long long)M * K, nw = (long long)N * K;
+    if (nx > kMaxElems || nw > kMaxElems) return fail(FCONV_EINVAL, "fgemm_lse_mish: a tensor has 2^31 or more elements");
+    const size_t ob = (size_t)M * 4;
+    if (overlaps(out, ob, x, nx * 4) || overlaps(out, ob, w, nw * 4) || overlaps(out, ob, b, (size_t)N * 4))
+        return fail(FCONV_EINVAL, "fgemm_lse_mish: out overlaps an input");
+
+    const fconv::GemmPlan plan = fconv::plan_gemm(M, K, N, x, w);
+    if ((long long)plan.tilesM * plan.tilesN > 0x7FFFFFFFLL)
+        return fail(FCONV_EUNSUPPORTED, "fgemm_lse_mish: launch grid too large");
+    void* ws = nullptr;
+    int rc = get_workspace(stream, plan.workspace_bytes(), &ws);
+    if (rc != FCONV_OK) return rc;
+    hipError_t e = fconv::launch_gemm_lse(plan, x, w, b, scale, cmin, cmax, out, ws, stream, active_timer());
+    if (e != hipSuccess) return fail(FCONV_EHIP, std::string("fgemm_lse_mish launch: ") + hipGetErrorString(e));
+    return ok();
+}
+
+FCONV_API int fconv_release(void) {
+    std::lock_guard<std::mutex> lock(g_ws_mutex);
+    int rc = FCONV_OK;
+    int cur = 0;
+    const bool have_dev = hipGetDevice(&cur) == hipSuccess;
+    for (auto& kv : g_ws) {
+        if (!kv.second.ptr) continue;
+        // A device-wide sync: the stream itself may already have been destroyed.
+        if (hipSetDevice(kv.first.first) != hipSuccess || hipDeviceSynchronize() != hipSuccess ||
+            hipFree(kv.second.ptr) != hipSuccess)
+            rc = fail(FCONV_EHIP, "fconv_release: HIP error while freeing a workspace");
+    }
+    g_ws.clear();
+    if (have_dev) (void)hipSetDevice(cur);
+    if (rc == FCONV_OK) return ok();
+    return rc;
+}
+
+FCONV_API int fconv_profile(int enable) {
+    int rc = g_timer.drain();
+    {
+        std::lock_guard<std::mutex> lock(g_timer.mu);
+        g_timer.totals.clear();
+        g_timer.enabled = enable != 0;
+    }
+    if (rc != FCONV_OK) return fail(rc, "fconv_profile: HIP error while draining events");
+    return ok();
+}
+
+FCONV_API int fconv_profile_read(const char* kernel, double* total_ms, long long* launches) {
+    if (!kernel || !total_ms || !launches) return fail(FCONV_EINVAL, "fconv_profile_read: null argument");
+    int rc = g_timer.drain();
+    if (rc != FCONV_OK) return fail(rc, "fconv_profile_read: HIP error while draining events");
+    std::lock_guard<std::mutex> lock(g_timer.mu);
+    auto it = g_timer.totals.find(kernel);
+    *total_ms = it == g_timer.totals.end() ? 0.0 : it->second.first;
+    *launches = it == g_timer.totals.end() ? 0 : it->second.second;
+    return ok();
+}

@@ -1,0 +1,243 @@
+// Fused GEMM + scale + clamp + row logsumexp + z*mish(z) for gfx950.
+//
+// Source: the Linear -> x2 -> x+x -> clamp -> logsumexp -> x*mish(x) model of the
+// "Kimi-K2.6 l2_p22" POPCORNBENCH page. The page materializes the GEMM output and
+// reduces it row by row; here the (M x N) product never leaves the chip:
+//   kernel 1 (gemm_lse_partials): one workgroup per BM x BN output tile computes
+//     the tile on fp32 MFMA (v_mfma_f32_16x16x4_f32, LDS double-buffered over K),
+//     applies bias, scale and clamp in registers and reduces each of its rows to a
+//     (max, sum exp(c - max)) pair, written to part[m][tile_n];
+//   kernel 2 (lse_merge_mish): one wave per row merges the pairs with the page's
+//     online logsumexp rule, M = max m_t, S = sum s_t e^(m_t - M), in a fixed
+//     order, then writes z * mish(z) with z = M + log S.
+// Both operands are K-contiguous (x [M][K], w [N][K]); LDS rows are 16 floats of
+// K plus 4 floats of padding (20-dword pitch: conflict-free 16-byte fragment reads).
+#include "device_math.h"
+#include "internal.h"
+
+namespace fconv {
+namespace {
+
+typedef float f4 __attribute__((ext_vector_type(4)));
+
+constexpr int kThreads = 256;
+constexpr int BK = 16;
+constexpr int kPitch = 20;  // floats per LDS row
+
+template <int BM_, int BN_, int WM_, int WN_>
+struct GTile {
+    static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_;
+    static constexpr int MB = BM / WM / 16;   // 16-row blocks per wave
+    static constexpr int NB = BN / WN / 16;   // 16-col blocks per wave
+    static constexpr int LA = BM * BK / 4 / kThreads;  // float4 loads per thread (A)
+    static constexpr int LB = BN * BK / 4 / kThreads;  // float4 loads per thread (B)
+    static_assert(WM * WN == kThreads / 64, "four waves");
+    static_assert(LA >= 1 && LB >= 1, "tile too small for the loader");
+};
+
+using GTileA = GTile<128, 128, 2, 2>;
+
+template <bool VEC>
+__device__ __forceinline__ f4 load4(const float* __restrict__ base, int rows, int K, int row, int k) {
+    // Four consecutive K elements of one row; out-of-range elements read as zero.
+    if (row >= rows) return f4{0.f, 0.f, 0.f, 0.f};
+    const float* p = base + (long long)row * K + k;
+    if constexpr (VEC) {
+        if (k < K) return *(const f4*)p;  // K % 4 == 0: the group is all in or all out
+        return f4{0.f, 0.f, 0.f, 0.f};
+    } else {
+        f4 v;
+        v.x = k < K ? p[0] : 0.f;
+        v.y = k + 1 < K ? p[1] : 0.f;
+        v.z = k + 2 < K ? p[2] : 0.f;
+        v.w = k + 3 < K ? p[3] : 0.f;
+        return v;
+    }
+}
+
+template <class TL, bool VEC>
+__global__ __launch_bounds__(kThreads) void gemm_lse_partials(
+    const float* __restrict__ X, const float* __restrict__ Wt, const float* __restrict__ bias,
+    float2* __restrict__ part, int M, int K, int N, float scale, float cmin, float cmax, int tilesN) {
+    __shared__ __attribute__((aligned(16))) float As[2][TL::BM * kPitch];
+    __shared__ __attribute__((aligned(16))) float Bs[2][TL::BN * kPitch];
+
+    const int tn = blockIdx.x % tilesN, tm = blockIdx.x / tilesN;
+    const int m0 = tm * TL::BM, n0 = tn * TL::BN;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int g = lane >> 4, i = lane & 15;
+    const int wm = wave % TL::WM, wn = wave / TL::WM;
+    const int rm0 = wm * TL::MB * 16, rn0 = wn * TL::NB * 16;
+
+    f4 acc[TL::MB][TL::NB];
+#pragma unroll
+    for (int a = 0; a < TL::MB; ++a)
+#pragma unroll
+        for (int b = 0; b < TL::NB; ++b) acc[a][b] = f4{0.f, 0.f, 0.f, 0.f};
+
+    f4 ra[TL::LA], rb[TL::LB];
+    auto gload = [&](int k0) {
+#pragma unroll
+        for (int j = 0; j < TL::LA; ++j) {
+            const int it = tid + j * kThreads;
+            ra[j] = load4<VEC>(X, M, K, m0 + (it >> 2), k0 + (it & 3) * 4);
+        }
+#pragma unroll
+        for (int j = 0; j < TL::LB; ++j) {
+            const int it = tid + j * kThreads;
+            rb[j] = load4<VEC>(Wt, N, K, n0 + (it >> 2), k0 + (it & 3) * 4);
+        }
+    };
+    auto sstore = [&](int buf) {
+#pragma unroll
+        for (int j = 0; j < TL::LA; ++j) {
+            const int it = tid + j * kThreads;
+            *(f4*)&As[buf][(it >> 2) * kPitch + (it & 3) * 4] = ra[j];
+        }
+#pragma unroll
+        for (int j = 0; j < TL::LB; ++j) {
+            const int it = tid + j * kThreads;
+            *(f4*)&Bs[buf][(it >> 2) * kPitch + (it & 3) * 4] = rb[j];
+        }
+    };
+
+    const int nk = (K + BK - 1) / BK;
+    gload(0);
+    sstore(0);
+    __syncthreads();
+    for (int kt = 0; kt < nk; ++kt) {
+        const int cur = kt & 1;
+        if (kt + 1 < nk) gload((kt + 1) * BK);
+        f4 a[TL::MB], b[TL::NB];
+#pragma unroll
+        for (int j = 0; j < TL::MB; ++j) a[j] = *(const f4*)&As[cur][(rm0 + j * 16 + i) * kPitch + 4 * g];
+#pragma unroll
+        for (int j = 0; j < TL::NB; ++j) b[j] = *(const f4*)&Bs[cur][(rn0 + j * 16 + i) * kPitch + 4 * g];
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+#pragma unroll
+            for (int jm = 0; jm < TL::MB; ++jm)
+#pragma unroll
+                for (int jn = 0; jn < TL::NB; ++jn)
+                    acc[jm][jn] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[jm][s], b[jn][s], acc[jm][jn], 0, 0, 0);
+        if (kt + 1 < nk) sstore(cur ^ 1);
+        __syncthreads();
+    }
+
+    // Epilogue: lane (g, i) register r holds row rm0 + 16 jm + 4g + r, column rn0 + 16 jn + i.
+    float bv[TL::NB];
+    bool cv[TL::NB];
+#pragma unroll
+    for (int jn = 0; jn < TL::NB; ++jn) {
+        const int n = n0 + rn0 + jn * 16 + i;
+        cv[jn] = n < N;
+        bv[jn] = cv[jn] ? bias[n] : 0.0f;
+    }
+    float rmax[TL::MB][4], rsum[TL::MB][4];
+#pragma unroll
+    for (int jm = 0; jm < TL::MB; ++jm) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            float mx = -INFINITY;
+#pragma unroll
+            for (int jn = 0; jn < TL::NB; ++jn) {
+                const float c = fminf(fmaxf(scale * (acc[jm][jn][r] + bv[jn]), cmin), cmax);
+                acc[jm][jn][r] = c;
+                mx = cv[jn] ? fmaxf(mx, c) : mx;
+            }
+#pragma unroll
+            for (int off = 8; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 64));
+            float s = 0.0f;
+#pragma unroll
+            for (int jn = 0; jn < TL::NB; ++jn) s += cv[jn] ? fast_exp(acc[jm][jn][r] - mx) : 0.0f;
+#pragma unroll
+            for (int off = 8; off >= 1; off >>= 1) s += __shfl_xor(s, off, 64);
+            rmax[jm][r] = mx;
+            rsum[jm][r] = s;
+        }
+    }
+    // Merge the WN column slices of each row through LDS (the main loop ended on a barrier).
+    float2* red = (float2*)&As[0][0];
+    if (i == 0) {
+#pragma unroll
+        for (int jm = 0; jm < TL::MB; ++jm)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                red[wn * TL::BM + rm0 + jm * 16 + 4 * g + r] = make_float2(rmax[jm][r], rsum[jm][r]);
+    }
+    __syncthreads();
+    if (tid < TL::BM && m0 + tid < M) {
+        float mx = -INFINITY;
+#pragma unroll
+        for (int w = 0; w < TL::WN; ++w) mx = fmaxf(mx, red[w * TL::BM + tid].x);
+        float s = 0.0f;
+#pragma unroll
+        for (int w = 0; w < TL::WN; ++w) {
+            const float2 p = red[w * TL::BM + tid];
+            s += p.y > 0.0f ? p.y * fast_exp(p.x - mx) : 0.0f;
+        }
+        part[(long long)(m0 + tid) * tilesN + tn] = make_float2(mx, s);
+    }
+}
+
+// One wave per row: fixed-order online-logsumexp merge of the tile partials, then
+// out = z * mish(z) with the overflow-free softplus max(z,0) + log1p(e^-|z|).
+__global__ __launch_bounds__(256) void lse_merge_mish(const float2* __restrict__ part,
+                                                      float* __restrict__ out, int M, int tilesN) {
+    const int row = (int)(((long long)blockIdx.x * blockDim.x + threadIdx.x) >> 6);
+    const int lane = threadIdx.x & 63;
+    if (row >= M) return;
+    const float2* p = part + (long long)row * tilesN;
+    float mx = -INFINITY;
+    for (int t = lane; t < tilesN; t += 64) mx = fmaxf(mx, p[t].x);
+    mx = wave_max(mx);
+    float s = 0.0f;
+    for (int t = lane; t < tilesN; t += 64) {
+        const float2 q = p[t];
+        s += q.y > 0.0f ? q.y * expf(q.x - mx) : 0.0f;
+    }
+    s = wave_sum(s);
+    if (lane == 0) {
+        const float z = mx + logf(s);
+        const float sp = fmaxf(z, 0.0f) + log1pf(expf(-fabsf(z)));
+        out[row] = z * (z * tanhf(sp));
+    }
+}
+
+}  // namespace
+
+GemmPlan plan_gemm(int M, int K, int N, const void* x, const void* w) {
+    GemmPlan p{};
+    p.M = M; p.K = K; p.N = N;
+    p.BM = GTileA::BM; p.BN = GTileA::BN;
+    p.tilesM = (M + p.BM - 1) / p.BM;
+    p.tilesN = (N + p.BN - 1) / p.BN;
+    p.vec = (K % 4 == 0) && (((size_t)x | (size_t)w) % 16 == 0);
+    p.part_bytes = (size_t)M * p.tilesN * sizeof(float2);
+    return p;
+}
+
+hipError_t launch_gemm_lse(const GemmPlan& p, const float* x, const float* w, const float* b, float scale,
+                           float cmin, float cmax, float* out, void* workspace, hipStream_t stream,
+                           KernelTimer* timer) {
+    float2* part = (float2*)workspace;
+    const unsigned grid = (unsigned)(p.tilesM * p.tilesN);
+    if (timer) timer->begin("gemm_lse_partials", stream);
+    if (p.vec)
+        hipLaunchKernelGGL((gemm_lse_partials<GTileA, true>), dim3(grid), dim3(kThreads), 0, stream, x, w, b,
+                           part, p.M, p.K, p.N, scale, cmin, cmax, p.tilesN);
+    else
+        hipLaunchKernelGGL((gemm_lse_partials<GTileA, false>), dim3(grid), dim3(kThreads), 0, stream, x, w, b,
+                           part, p.M, p.K, p.N, scale, cmin, cmax, p.tilesN);
+    hipError_t e = hipGetLastError();
+    if (timer) timer->end("gemm_lse_partials", stream);
+    if (e != hipSuccess) return e;
+    if (timer) timer->begin("lse_merge_mish", stream);
+    hipLaunchKernelGGL(lse_merge_mish, dim3((unsigned)((p.M + 3) / 4)), dim3(256), 0, stream,
+                       (const float2*)part, out, p.M, p.tilesN);
+    e = hipGetLastError();
+    if (timer) timer->end("lse_merge_mish", stream);
+    return e;
+}
+
+}  // namespace fconv

@@ -1,0 +1,49 @@
+// Internal launch interface between the C ABI (capi.hip) and the kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <cstddef>
+
+namespace fconv {
+
+// Optional per-kernel timing: when non-null, launchers bracket each kernel with
+// begin(name) / end(name), which record HIP events on the launch stream.
+struct KernelTimer {
+    virtual void begin(const char* kernel, hipStream_t s) = 0;
+    virtual void end(const char* kernel, hipStream_t s) = 0;
+    virtual ~KernelTimer() = default;
+};
+
+// Conv: workspace = repacked weights followed by (pool only) per-tile partial sums.
+struct ConvPlan {
+    bool bf16;
+    int act, pool;
+    int N, Cin, H, W, Cout;
+    int OH, OW;
+    int tile_cfg;            // index of the tile configuration used
+    int TH, TW, BN, CK;      // output tile rows/cols, oc per workgroup, channels per K chunk
+    int tilesH, tilesW, ocTiles, nChunk, CoutPad;
+    size_t wpack_bytes;      // repacked weights [nChunk][9][CoutPad][CK]
+    size_t part_bytes;       // pool partials [N][Cout][tilesH * tilesW] fp32
+    size_t workspace_bytes() const { return wpack_bytes + part_bytes; }
+    long long grid() const { return (long long)N * tilesH * tilesW * ocTiles; }
+};
+
+ConvPlan plan_conv(bool bf16, int act, int pool, int N, int Cin, int H, int W, int Cout);
+hipError_t launch_conv(const ConvPlan& p, const void* x, const void* w, const float* b,
+                       float* out, void* workspace, hipStream_t stream, KernelTimer* timer);
+
+struct GemmPlan {
+    int M, K, N;
+    int BM, BN;
+    int tilesM, tilesN;
+    bool vec;                // K % 4 == 0 and 16-byte aligned rows: dwordx4 loads
+    size_t part_bytes;       // [M][tilesN] (max, sum) pairs
+    size_t workspace_bytes() const { return part_bytes; }
+};
+
+GemmPlan plan_gemm(int M, int K, int N, const void* x, const void* w);
+hipError_t launch_gemm_lse(const GemmPlan& p, const float* x, const float* w, const float* b,
+                           float scale, float cmin, float cmax, float* out, void* workspace,
+                           hipStream_t stream, KernelTimer* timer);
+
+}  // namespace fconv

@@ -1,0 +1,131 @@
+/*
+ * fconv -- fused dense-contraction + epilogue kernels for AMD Instinct MI355X (gfx950).
+ *
+ * Two fused operations, each computed in one pass so the full-resolution
+ * intermediate never goes through HBM:
+ *
+ *   fconv_act_pool  3x3 valid stride-1 Conv2d + bias -> GELU (erf) or Mish(Mish(.))
+ *                   -> optional global average pool.
+ *   fgemm_lse_mish  Linear (x W^T + b) -> scale -> clamp -> row logsumexp -> z*mish(z).
+ *
+ * Error behaviour (all entry points): arguments are validated on the host before any
+ * HIP call; a bad argument returns FCONV_EINVAL with nothing enqueued. A HIP failure
+ * (allocation of the library's workspace, a launch) returns FCONV_ENOMEM / FCONV_EHIP.
+ * fconv_last_error() returns a readable message for the calling thread's last non-OK
+ * return. No entry point synchronizes the host with the stream.
+ *
+ * Ownership: every tensor pointer is a DEVICE pointer owned by the caller; outputs are
+ * preallocated by the caller and must not alias any input. The library owns a small
+ * device workspace per (device, stream) pair -- repacked weights and per-tile partial
+ * results -- which it grows on demand (the growth path synchronizes that stream) and
+ * frees in fconv_release(). Calls on one stream are ordered by the stream; calls that
+ * pass the same stream from several host threads must be serialized by the caller.
+ */
+#ifndef FCONV_H
+#define FCONV_H
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+    FCONV_OK = 0,
+    FCONV_EINVAL = -1,       /* bad argument; nothing was enqueued                   */
+    FCONV_EUNSUPPORTED = -2, /* valid request this build does not implement          */
+    FCONV_EHIP = -3,         /* a HIP runtime call or kernel launch failed           */
+    FCONV_ENOMEM = -4        /* the workspace could not be allocated                 */
+};
+
+/* `act` argument of fconv_act_pool: bits 0..7 pick the activation, bits 8..11 the
+ * element type of x and w. Every other bit must be zero. */
+enum {
+    FCONV_ACT_NONE = 0,   /* identity (plain conv + bias)                                 */
+    FCONV_ACT_GELU = 1,   /* 0.5 v (1 + erf(v / sqrt 2)), the exact form                  */
+    FCONV_ACT_MISH2 = 2,  /* mish(mish(v)), mish(v) = v tanh(log(1 + e^v))                */
+    FCONV_DT_F32 = 0x000, /* x, w float32                                                 */
+    FCONV_DT_BF16 = 0x100 /* x, w bfloat16 (products exact in fp32, fp32 accumulation)    */
+};
+
+/*
+ * Fused 3x3 convolution + bias + activation (+ global average pool).
+ *
+ * Computes, for 0 <= oh < H-2 and 0 <= ow < W-2 (stride 1, no padding, no kernel flip):
+ *   pre[n,oc,oh,ow] = b[oc] + sum_{ic<Cin, kh<3, kw<3} w[oc,ic,kh,kw] * x[n,ic,oh+kh,ow+kw]
+ *   pool == 0:  out[n,oc,oh,ow] = act(pre[n,oc,oh,ow])
+ *   pool == 1:  out[n,oc]       = (1 / ((H-2)(W-2))) * sum_{oh,ow} act(pre[n,oc,oh,ow])
+ * Sources: the direct-convolution sum and the Conv2d -> Mish -> Mish chain of the
+ * "Kimi-K2.6 l2_p4" POPCORNBENCH page; the exact GELU and the AdaptiveAvgPool2d(1)
+ * mean of the "Kimi-K2.6 l2_p67" page.
+ *
+ *   x     [N][Cin][H][W]      NCHW contiguous, float32 or bfloat16 (see `act`)
+ *   w     [Cout][Cin][3][3]   OIHW contiguous, same element type as x
+ *   b     [Cout]              float32
+ *   out   pool=1: [N][Cout] float32;  pool=0: [N][Cout][H-2][W-2] float32 (NCHW)
+ *   act   FCONV_ACT_* | FCONV_DT_*
+ *   pool  0 or 1
+ *   stream  HIP stream the work is enqueued on (0 = the null stream)
+ *
+ * Returns FCONV_EINVAL for a null pointer, N, Cin or Cout < 1, H or W < 3, an unknown
+ * act/dtype bit, pool not in {0,1}, a tensor of 2^31 or more elements, or an output
+ * that overlaps an input. The pooled result is deterministic run to run (no atomics).
+ */
+int fconv_act_pool(const void* x, const void* w, const float* b,
+                   int N, int Cin, int H, int W, int Cout,
+                   int act, int pool, float* out, hipStream_t stream);
+
+/*
+ * Fused GEMM + scale + clamp + row logsumexp + z*mish(z).
+ *
+ *   y[m,j] = scale * (sum_k x[m,k] * w[j,k] + b[j])
+ *   c[m,j] = min(max(y[m,j], cmin), cmax)
+ *   z[m]   = log(sum_j exp(c[m,j]))        (evaluated max-shifted, tile by tile)
+ *   out[m] = z[m] * mish(z[m])
+ * Source: the Linear -> x2 -> x+x -> clamp -> logsumexp -> x*mish(x) model of the
+ * "Kimi-K2.6 l2_p22" POPCORNBENCH page (its x2 then x+x is scale = 4) and the page's
+ * online max / sum-of-exponentials merge rule.
+ *
+ *   x    [M][K] row-major float32
+ *   w    [N][K] row-major float32 (nn.Linear weight layout)
+ *   b    [N] float32
+ *   out  [M] float32 (the (M, 1) result)
+ *
+ * Returns FCONV_EINVAL for a null pointer, M, K or N < 1, a non-finite scale, cmin or
+ * cmax, cmin > cmax, a tensor of 2^31 or more elements, or an output overlapping an
+ * input. The result is deterministic run to run (fixed-order merge, no atomics).
+ */
+int fgemm_lse_mish(const float* x, const float* w, const float* b,
+                   int M, int K, int N, float scale, float cmin, float cmax,
+                   float* out, hipStream_t stream);
+
+/* Message describing the calling thread's last non-OK return ("" if none). The
+ * pointer stays valid until the next call into the library from that thread. */
+const char* fconv_last_error(void);
+
+/* Synchronizes every device that holds a workspace, frees all workspaces and
+ * returns FCONV_OK (or FCONV_EHIP). Later calls allocate afresh. */
+int fconv_release(void);
+
+/*
+ * Per-kernel timing, for measurement tools. fconv_profile(1) makes every later call
+ * bracket each of its kernels with HIP events recorded on the call's stream (a small
+ * host cost per launch); fconv_profile(0) stops it. Either call first waits for the
+ * outstanding events and clears the accumulated totals.
+ * fconv_profile_read(kernel, &ms, &launches) waits for the recorded events and returns
+ * the summed event time in milliseconds and the number of launches of `kernel` since
+ * the last fconv_profile() call. Kernel names: "pack_weights", "conv3x3_fused",
+ * "pool_finalize", "gemm_lse_partials", "lse_merge_mish". Unknown names read as zero.
+ * Returns FCONV_EINVAL for a null argument, FCONV_EHIP if an event wait fails.
+ */
+int fconv_profile(int enable);
+int fconv_profile_read(const char* kernel, double* total_ms, long long* launches);
+
+/* Library ABI version (major * 100 + minor). */
+int fconv_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FCONV_H */

@@ -14,8 +14,12 @@ def pytest_configure(config):
 
 
 @pytest.fixture(scope="session", autouse=True)
-def _oracle_built():
+def _libraries_built():
+    # Normally built beforehand by __graft_entry__.build(); build here only if absent.
     import oracle
     if not os.path.exists(oracle._LIB):
         oracle.build()
+    from gemm_activation_reduction_amd import LIB_PATH, build
+    if not os.path.exists(LIB_PATH):
+        build.build()
     yield

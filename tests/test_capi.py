@@ -1,0 +1,108 @@
+"""C-ABI library checks that need no GPU: every symbol the header declares is exported,
+host-side validation rejects bad arguments before any HIP call, only one HIP runtime is
+mapped, and the product path never touches the oracle."""
+import os
+import re
+import subprocess
+
+import pytest
+
+import gemm_activation_reduction_amd as fc
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fconv.h")
+S0 = 0  # explicit null stream: the default (torch's current stream) needs a GPU
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_expected_api():
+    assert declared_functions() == sorted(fc.EXPORTS)
+
+
+def test_every_declared_symbol_is_exported():
+    out = subprocess.run(["nm", "-D", "--defined-only", fc.LIB_PATH], check=True,
+                         stdout=subprocess.PIPE).stdout.decode()
+    exported = {l.split()[-1] for l in out.splitlines() if " T " in l}
+    for name in declared_functions():
+        assert name in exported, name
+    lib = fc.load_library()
+    for name in declared_functions():
+        assert getattr(lib, name) is not None
+    assert fc.fconv_version() == 100
+
+
+def test_single_hip_runtime_mapped():
+    fc.load_library()
+    assert len(fc.loaded_hip_runtimes()) == 1, fc.loaded_hip_runtimes()
+
+
+def test_library_does_not_link_the_oracle():
+    out = subprocess.run(["ldd", fc.LIB_PATH], stdout=subprocess.PIPE).stdout.decode()
+    assert "oracle" not in out
+    pkg = os.path.join(ROOT, "gemm_activation_reduction_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".h", ".cpp")):
+                src = open(os.path.join(dirpath, f)).read()
+                assert not re.search(r"^\s*(import|from)\s+oracle\b", src, flags=re.M), f
+                assert "liboracle" not in src, f
+
+
+FAKE = 1 << 40  # plausible, never dereferenced: validation fails before any HIP call
+
+
+def conv_err(**kw):
+    args = dict(x=FAKE, w=FAKE + (1 << 30), b=FAKE + (2 << 30), N=2, Cin=3, H=16, W=16, Cout=8,
+                act=fc.ACT_GELU, pool=1, out=FAKE + (3 << 30))
+    args.update(kw)
+    with pytest.raises(fc.FconvError) as e:
+        fc.fconv_act_pool(args["x"], args["w"], args["b"], args["N"], args["Cin"], args["H"], args["W"],
+                          args["Cout"], args["act"], args["pool"], args["out"], S0)
+    return e.value
+
+
+@pytest.mark.parametrize("kw,frag", [
+    (dict(x=0), "null"), (dict(w=0), "null"), (dict(b=0), "null"), (dict(out=0), "null"),
+    (dict(N=0), ">= 1"), (dict(Cin=-1), ">= 1"), (dict(Cout=0), ">= 1"),
+    (dict(H=2), ">= 3"), (dict(W=1), ">= 3"),
+    (dict(act=3), "unknown activation"), (dict(act=0x200 | 1), "dtype"), (dict(act=0x1000), "dtype"),
+    (dict(pool=2), "pool"), (dict(pool=-1), "pool"),
+    (dict(N=1 << 16, Cin=1 << 8, H=1 << 8, W=1 << 8), "2^31"),
+    (dict(out=FAKE + 64), "overlaps"), (dict(out=FAKE + (1 << 30) + 100), "overlaps"),
+])
+def test_conv_validation(kw, frag):
+    e = conv_err(**kw)
+    assert e.code == fc.FCONV_EINVAL
+    assert frag in e.message
+
+
+def gemm_err(**kw):
+    args = dict(x=FAKE, w=FAKE + (1 << 30), b=FAKE + (2 << 30), M=4, K=8, N=16, scale=4.0, cmin=-10.0,
+                cmax=10.0, out=FAKE + (3 << 30))
+    args.update(kw)
+    with pytest.raises(fc.FconvError) as e:
+        fc.fgemm_lse_mish(args["x"], args["w"], args["b"], args["M"], args["K"], args["N"], args["scale"],
+                          args["cmin"], args["cmax"], args["out"], S0)
+    return e.value
+
+
+@pytest.mark.parametrize("kw,frag", [
+    (dict(x=0), "null"), (dict(out=0), "null"), (dict(M=0), ">= 1"), (dict(K=-3), ">= 1"), (dict(N=0), ">= 1"),
+    (dict(scale=float("inf")), "scale"), (dict(scale=float("nan")), "scale"),
+    (dict(cmin=1.0, cmax=-1.0), "cmin"), (dict(cmin=float("nan")), "cmin"),
+    (dict(M=1 << 20, K=1 << 12), "2^31"), (dict(out=FAKE + 8), "overlaps"),
+])
+def test_gemm_validation(kw, frag):
+    e = gemm_err(**kw)
+    assert e.code == fc.FCONV_EINVAL
+    assert frag in e.message
+
+
+def test_last_error_is_per_call():
+    conv_err(N=0)
+    assert ">= 1" in fc.fconv_last_error()

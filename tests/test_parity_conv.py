@@ -1,0 +1,164 @@
+"""GPU parity of fconv_act_pool against the fp64 CPU oracle (called through the C ABI).
+
+Small and ragged shapes are compared element by element against the full oracle;
+the full-size workloads (in the launch configuration the benchmark times) are compared
+on sampled outputs the oracle computes one by one. Tolerance: max |g - o| / (1 + |o|)
+<= 1e-4 for fp32 inputs and 2e-2 for bf16 inputs.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from tests._util import TOL_BF16, TOL_F32, max_rel_err, to_device, workload_conv_inputs
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+import gemm_activation_reduction_amd as fc  # noqa: E402
+
+
+def run_conv(x, w, b, act, pool, bf16=False, stream=None):
+    xd, wd, bd = to_device(x, bf16), to_device(w, bf16), to_device(b)
+    out = fc.conv_act_pool(xd, wd, bd, act=act, pool=bool(pool), stream=stream)
+    torch.cuda.synchronize()
+    return out.cpu().numpy()
+
+
+def rand_case(seed, N, Cin, H, W, Cout, bf16=False):
+    spec = dict(N=N, Cin=Cin, H=H, W=W, Cout=Cout, x_dist=("normal",), w_bound=1.0 / np.sqrt(9 * Cin),
+                b_bound=0.1, dtype="bf16" if bf16 else "f32")
+    return synth.conv_inputs(spec, seed_cfg=1000 + seed)
+
+
+SHAPES = [
+    (2, 3, 16, 16, 8),     # the tiny workload's shape
+    (3, 5, 37, 37, 19),    # odd everything: ragged tiles, channel and oc tails
+    (1, 1, 3, 3, 1),       # smallest valid input
+    (2, 17, 11, 40, 65),   # Cin one past a chunk, Cout one past an oc tile, OW % 4 == 2
+    (1, 16, 36, 34, 64),   # OW = 32: exactly one tile column, OW % 4 == 0
+    (1, 7, 3, 70, 5),      # a single output row
+    (2, 33, 20, 21, 16),   # Cin one past a bf16 chunk, odd OW
+]
+
+
+@pytest.mark.parametrize("bf16", [False, True])
+@pytest.mark.parametrize("act", [fc.ACT_NONE, fc.ACT_GELU, fc.ACT_MISH2])
+@pytest.mark.parametrize("pool", [0, 1])
+@pytest.mark.parametrize("shape", SHAPES)
+def test_conv_small_shapes_full_compare(shape, pool, act, bf16):
+    x, w, b = rand_case(hash(shape) % 997, *shape, bf16=bf16)
+    got = run_conv(x, w, b, act, pool, bf16)
+    ref = oracle.conv_act_pool(x, w, b, act, pool)
+    err = max_rel_err(got, ref)
+    print(f"shape={shape} pool={pool} act={act} bf16={bf16} err={err:.3e}", flush=True)
+    assert err <= (TOL_BF16 if bf16 else TOL_F32)
+
+
+def test_conv_tiny_workload():
+    x, w, b = workload_conv_inputs("conv_tiny")
+    got = run_conv(x, w, b, fc.ACT_GELU, 1)
+    ref = oracle.conv_act_pool(x, w, b, fc.ACT_GELU, 1)
+    assert got.shape == (2, 8)
+    assert max_rel_err(got, ref) <= TOL_F32
+
+
+def test_conv_shifted_delta_kernels_exact():
+    # w[oc, ic, kh, kw] = [oc == ic][kh == a][kw == c], b = 0, act none -> a shifted copy of x
+    N, C, H, W = 2, 20, 21, 35
+    x = synth.normal(4242, N * C * H * W).reshape(N, C, H, W)
+    for a in range(3):
+        for c in range(3):
+            w = np.zeros((C, C, 3, 3), np.float32)
+            for k in range(C):
+                w[k, k, a, c] = 1.0
+            got = run_conv(x, w, np.zeros(C, np.float32), fc.ACT_NONE, 0)
+            np.testing.assert_array_equal(got, x[:, :, a:a + H - 2, c:c + W - 2])
+
+
+def test_conv_zero_weights_and_constant_map():
+    N, Cin, H, W, Cout = 2, 16, 30, 30, 32
+    b = synth.uniform(77, Cout, -2.0, 2.0)
+    x = synth.normal(78, N * Cin * H * W).reshape(N, Cin, H, W)
+    w0 = np.zeros((Cout, Cin, 3, 3), np.float32)
+    for act in (fc.ACT_GELU, fc.ACT_MISH2):
+        expect = np.array([oracle.act(float(v), act) for v in b])
+        got = run_conv(x, w0, b, act, 1)
+        assert max_rel_err(got, np.broadcast_to(expect, got.shape)) <= TOL_F32
+        full = run_conv(x, w0, b, act, 0)
+        assert max_rel_err(full, np.broadcast_to(expect[None, :, None, None], full.shape)) <= TOL_F32
+    xc = np.full((N, Cin, H, W), 0.5, np.float32)
+    w = synth.uniform(79, Cout * Cin * 9, -0.1, 0.1).reshape(Cout, Cin, 3, 3)
+    pre = b.astype(np.float64) + 0.5 * w.astype(np.float64).sum(axis=(1, 2, 3))
+    for act in (fc.ACT_GELU, fc.ACT_MISH2):
+        got = run_conv(xc, w, b, act, 1)
+        expect = np.array([oracle.act(float(v), act) for v in pre])
+        assert max_rel_err(got, np.broadcast_to(expect, got.shape)) <= TOL_F32
+
+
+def test_conv_deterministic_and_stream():
+    x, w, b = rand_case(5, 4, 16, 60, 60, 64)
+    xd, wd, bd = to_device(x), to_device(w), to_device(b)
+    o1 = fc.conv_act_pool(xd, wd, bd, act="gelu", pool=True)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        o2 = fc.conv_act_pool(xd, wd, bd, act="gelu", pool=True, stream=s)
+    s.synchronize()
+    torch.cuda.synchronize()
+    o3 = fc.conv_act_pool(xd, wd, bd, act="gelu", pool=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(o1, o3)
+
+
+def sample_pairs(N, Cout, count, seed):
+    r = np.random.default_rng(seed)
+    n = r.integers(0, N, count)
+    oc = r.integers(0, Cout, count)
+    n[:2], oc[:2] = (0, N - 1), (0, Cout - 1)  # both corners of the (n, oc) grid
+    return n, oc
+
+
+@pytest.mark.parametrize("name,count", [("conv_gelu_pool_f32", 96), ("conv_gelu_pool_bf16", 48)])
+def test_conv_full_size_pooled_sampled(name, count):
+    spec = synth.CONV_WORKLOADS[name]
+    bf16 = spec["dtype"] == "bf16"
+    x, w, b = workload_conv_inputs(name)
+    print(f"{name}: running GPU", flush=True)
+    got = run_conv(x, w, b, spec["act"], 1, bf16)
+    assert got.shape == (spec["N"], spec["Cout"])
+    assert np.all(np.isfinite(got))
+    n, oc = sample_pairs(spec["N"], spec["Cout"], count, 3)
+    ref = oracle.conv_pool_sample(x, w, b, spec["act"], n, oc)
+    err = max_rel_err(got[n, oc], ref)
+    print(f"{name}: sampled err={err:.3e}", flush=True)
+    assert err <= (TOL_BF16 if bf16 else TOL_F32)
+
+
+def test_conv_full_size_mish2_full_output_sampled():
+    name = "conv_mish2_full_f32"
+    spec = synth.CONV_WORKLOADS[name]
+    x, w, b = workload_conv_inputs(name)
+    xd, wd, bd = to_device(x), to_device(w), to_device(b)
+    print(f"{name}: running GPU", flush=True)
+    out = fc.conv_act_pool(xd, wd, bd, act="mish2", pool=False)
+    torch.cuda.synchronize()
+    N, Cout, OH, OW = out.shape
+    assert (N, Cout, OH, OW) == (32, 128, 190, 190)
+    assert bool(torch.isfinite(out).all())
+    r = np.random.default_rng(4)
+    cnt = 20000
+    n, oc = r.integers(0, N, cnt), r.integers(0, Cout, cnt)
+    oh, ow = r.integers(0, OH, cnt), r.integers(0, OW, cnt)
+    # always include the four corners of the first and last maps and a full last row
+    extra = [(0, 0, 0, 0), (0, 0, OH - 1, OW - 1), (N - 1, Cout - 1, 0, OW - 1), (N - 1, Cout - 1, OH - 1, 0)]
+    extra += [(N - 1, Cout - 1, OH - 1, c) for c in range(OW)]
+    n = np.concatenate([n, [e[0] for e in extra]])
+    oc = np.concatenate([oc, [e[1] for e in extra]])
+    oh = np.concatenate([oh, [e[2] for e in extra]])
+    ow = np.concatenate([ow, [e[3] for e in extra]])
+    idx = [torch.from_numpy(a.astype(np.int64)).cuda() for a in (n, oc, oh, ow)]
+    got = out[idx[0], idx[1], idx[2], idx[3]].cpu().numpy()
+    ref = oracle.conv_point_sample(x, w, b, fc.ACT_MISH2, n, oc, oh, ow)
+    err = max_rel_err(got, ref)
+    print(f"{name}: sampled err={err:.3e}", flush=True)
+    assert err <= TOL_F32

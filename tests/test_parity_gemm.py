@@ -1,0 +1,93 @@
+"""GPU parity of fgemm_lse_mish against the fp64 CPU oracle (called through the C ABI).
+Tolerance: max |g - o| / (1 + |o|) <= 1e-4 (fp32)."""
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from tests._util import TOL_F32, max_rel_err, to_device, workload_gemm_inputs
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+import gemm_activation_reduction_amd as fc  # noqa: E402
+
+
+def run_gemm(X, W, b, scale=4.0, cmin=-10.0, cmax=10.0, stream=None):
+    out = fc.gemm_lse_mish(to_device(X), to_device(W), to_device(b), scale, cmin, cmax, stream=stream)
+    torch.cuda.synchronize()
+    return out.cpu().numpy()[:, 0]
+
+
+def rand_case(seed, M, K, N, wb=None):
+    wb = wb if wb is not None else 1.0 / math.sqrt(K)
+    return synth.gemm_inputs(dict(M=M, K=K, N=N, w_bound=wb, b_bound=wb), seed_cfg=2000 + seed)
+
+
+@pytest.mark.parametrize("M,K,N", [(37, 19, 53), (1, 1, 1), (5, 4, 3), (128, 128, 128), (130, 260, 300),
+                                   (64, 1000, 129), (257, 33, 1000), (3, 4096, 6144)])
+@pytest.mark.parametrize("scale,cmin,cmax", [(4.0, -10.0, 10.0), (4.0, -0.25, 0.5), (-3.0, -1e30, 1e30)])
+def test_gemm_small_shapes(M, K, N, scale, cmin, cmax):
+    X, W, b = rand_case(M + K + N, M, K, N)
+    got = run_gemm(X, W, b, scale, cmin, cmax)
+    ref, _ = oracle.gemm_lse_mish(X, W, b, scale, cmin, cmax)
+    err = max_rel_err(got, ref)
+    print(f"M={M} K={K} N={N} scale={scale} clamp=[{cmin},{cmax}] err={err:.3e}", flush=True)
+    assert err <= TOL_F32
+
+
+def test_gemm_constant_rows_closed_form():
+    M, K, N = 70, 16, 6144
+    X = np.ones((M, K), np.float32)
+    W = np.zeros((N, K), np.float32)
+    for beta in (0.0, 0.3, 5.0):
+        b = np.full(N, beta, np.float32)
+        got = run_gemm(X, W, b)
+        c = min(max(4.0 * float(np.float32(beta)), -10.0), 10.0)
+        z = c + math.log(N)
+        expect = z * z * math.tanh(math.log1p(math.exp(z)))
+        assert max_rel_err(got, np.full(M, expect)) <= TOL_F32
+
+
+def test_gemm_all_clamped_magnitude():
+    # every value clamps at 10 over 8192 columns: z = 10 + ln 8192 ~ 19, out ~ 361
+    M, K, N = 8, 8, 8192
+    got = run_gemm(np.ones((M, K), np.float32), np.ones((N, K), np.float32), np.zeros(N, np.float32))
+    ref, _ = oracle.gemm_lse_mish(np.ones((M, K), np.float32), np.ones((N, K), np.float32),
+                                  np.zeros(N, np.float32), 4.0, -10.0, 10.0)
+    assert max_rel_err(got, ref) <= TOL_F32
+    assert np.all(np.abs(got - 361.0) < 1.0)
+
+
+def test_gemm_deterministic_and_stream():
+    X, W, b = rand_case(9, 300, 512, 1000)
+    xd, wd, bd = to_device(X), to_device(W), to_device(b)
+    o1 = fc.gemm_lse_mish(xd, wd, bd)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        o2 = fc.gemm_lse_mish(xd, wd, bd, stream=s)
+    s.synchronize()
+    o3 = fc.gemm_lse_mish(xd, wd, bd)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(o1, o3)
+
+
+def test_gemm_full_size_sampled_rows():
+    name = "gemm_lse_mish_f32"
+    spec = synth.GEMM_WORKLOADS[name]
+    X, W, b = workload_gemm_inputs(name)
+    print(f"{name}: running GPU", flush=True)
+    got = run_gemm(X, W, b, spec["scale"], spec["cmin"], spec["cmax"])
+    assert got.shape == (spec["M"],) and np.all(np.isfinite(got))
+    r = np.random.default_rng(6)
+    rows = np.unique(np.concatenate([[0, spec["M"] - 1], r.integers(0, spec["M"], 62)]))
+    ref, z = oracle.gemm_lse_mish(X, W, b, spec["scale"], spec["cmin"], spec["cmax"], rows=rows)
+    err = max_rel_err(got[rows], ref)
+    print(f"{name}: sampled err={err:.3e} z range [{z.min():.3f}, {z.max():.3f}]", flush=True)
+    assert err <= TOL_F32
+    # LSE bounds hold for every row (property at full size, no oracle needed)
+    lo, hi = spec["cmin"] + math.log(spec["N"]), spec["cmax"] + math.log(spec["N"])
+    zz_lo, zz_hi = lo * lo * math.tanh(math.log1p(math.exp(lo))), hi * hi
+    assert np.all(got >= min(zz_lo, 0.0) - 1e-3) and np.all(got <= zz_hi + 1e-3)
