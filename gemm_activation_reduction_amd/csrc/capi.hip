@@ -33,38 +33,59 @@ constexpr long long kMaxElems = (1LL << 31) - 1;
 struct Workspace {
     void* ptr = nullptr;
     size_t bytes = 0;
+    unsigned* counters = nullptr;  // zero between calls: each kernel resets what it used
+    int ncounters = 0;
 };
 
 std::mutex g_ws_mutex;
 std::map<std::pair<int, hipStream_t>, Workspace> g_ws;
 
-// Returns a device buffer of at least `bytes` owned by the library for (device, stream).
-// Growth waits for the stream (earlier work may still use the old buffer) before freeing.
-int get_workspace(hipStream_t stream, size_t bytes, void** out) {
+// Returns device buffers owned by the library for (device, stream): a scratch area of at
+// least `bytes` and `ncounters` zero-initialized counter words. Growth waits for the
+// stream (earlier work may still use the old buffers) before freeing.
+int get_workspace(hipStream_t stream, size_t bytes, int ncounters, void** out, unsigned** counters) {
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return fail(FCONV_EHIP, std::string("hipGetDevice: ") + hipGetErrorString(e));
     std::lock_guard<std::mutex> lock(g_ws_mutex);
     Workspace& ws = g_ws[std::make_pair(dev, stream)];
-    if (ws.bytes < bytes) {
-        if (ws.ptr) {
+    if (ws.bytes < bytes || ws.ncounters < ncounters) {
+        if (ws.ptr || ws.counters) {
             e = hipStreamSynchronize(stream);
             if (e != hipSuccess)
                 return fail(FCONV_EHIP, std::string("hipStreamSynchronize: ") + hipGetErrorString(e));
+        }
+        if (ws.bytes < bytes) {
             (void)hipFree(ws.ptr);
             ws.ptr = nullptr;
             ws.bytes = 0;
+            size_t want = bytes < (1u << 20) ? (1u << 20) : bytes;
+            e = hipMalloc(&ws.ptr, want);
+            if (e != hipSuccess) {
+                ws.ptr = nullptr;
+                (void)hipGetLastError();
+                return fail(FCONV_ENOMEM, "workspace hipMalloc(" + std::to_string(want) + "): " + hipGetErrorString(e));
+            }
+            ws.bytes = want;
         }
-        size_t want = bytes < (1u << 20) ? (1u << 20) : bytes;
-        e = hipMalloc(&ws.ptr, want);
-        if (e != hipSuccess) {
-            ws.ptr = nullptr;
-            (void)hipGetLastError();
-            return fail(FCONV_ENOMEM, "workspace hipMalloc(" + std::to_string(want) + "): " + hipGetErrorString(e));
+        if (ws.ncounters < ncounters) {
+            (void)hipFree(ws.counters);
+            ws.counters = nullptr;
+            ws.ncounters = 0;
+            int want = ncounters < 4096 ? 4096 : ncounters;
+            e = hipMalloc(&ws.counters, (size_t)want * sizeof(unsigned));
+            if (e == hipSuccess) e = hipMemset(ws.counters, 0, (size_t)want * sizeof(unsigned));
+            if (e != hipSuccess) {
+                (void)hipFree(ws.counters);
+                ws.counters = nullptr;
+                (void)hipGetLastError();
+                return fail(FCONV_ENOMEM, std::string("workspace counters: ") + hipGetErrorString(e));
+            }
+            ws.ncounters = want;
         }
-        ws.bytes = want;
     }
     *out = ws.ptr;
+    if (counters) *counters = ws.counters;
     return FCONV_OK;
 }
 
@@ -156,8 +177,11 @@ FCONV_API int fconv_act_pool(const void* x, const void* w, const float* b, int N
 
     const fconv::ConvPlan plan = fconv::plan_conv(dt == FCONV_DT_BF16, kind, pool, N, Cin, H, W, Cout);
     if (plan.grid() > 0x7FFFFFFFLL) return fail(FCONV_EUNSUPPORTED, "fconv_act_pool: launch grid too large");
+    // The kernels address one image of x, and the repacked weights, with 32-bit byte offsets.
+    if ((long long)Cin * H * W * (long long)esz > 0x7FFF0000LL || (long long)plan.wpack_bytes > 0x7FFF0000LL)
+        return fail(FCONV_EUNSUPPORTED, "fconv_act_pool: one image (or the weights) exceeds 2 GiB");
     void* ws = nullptr;
-    int rc = get_workspace(stream, plan.workspace_bytes(), &ws);
+    int rc = get_workspace(stream, plan.workspace_bytes(), 0, &ws, nullptr);
     if (rc != FCONV_OK) return rc;
     hipError_t e = fconv::launch_conv(plan, x, w, b, out, ws, stream, active_timer());
     if (e != hipSuccess) return fail(FCONV_EHIP, std::string("fconv_act_pool launch: ") + hipGetErrorString(e));
@@ -181,7 +205,7 @@ FCONV_API int fgemm_lse_mish(const float* x, const float* w, const float* b, int
     if ((long long)plan.tilesM * plan.tilesN > 0x7FFFFFFFLL)
         return fail(FCONV_EUNSUPPORTED, "fgemm_lse_mish: launch grid too large");
     void* ws = nullptr;
-    int rc = get_workspace(stream, plan.workspace_bytes(), &ws);
+    int rc = get_workspace(stream, plan.workspace_bytes(), 0, &ws, nullptr);
     if (rc != FCONV_OK) return rc;
     hipError_t e = fconv::launch_gemm_lse(plan, x, w, b, scale, cmin, cmax, out, ws, stream, active_timer());
     if (e != hipSuccess) return fail(FCONV_EHIP, std::string("fgemm_lse_mish launch: ") + hipGetErrorString(e));
@@ -194,10 +218,10 @@ FCONV_API int fconv_release(void) {
     int cur = 0;
     const bool have_dev = hipGetDevice(&cur) == hipSuccess;
     for (auto& kv : g_ws) {
-        if (!kv.second.ptr) continue;
+        if (!kv.second.ptr && !kv.second.counters) continue;
         // A device-wide sync: the stream itself may already have been destroyed.
         if (hipSetDevice(kv.first.first) != hipSuccess || hipDeviceSynchronize() != hipSuccess ||
-            hipFree(kv.second.ptr) != hipSuccess)
+            hipFree(kv.second.ptr) != hipSuccess || hipFree(kv.second.counters) != hipSuccess)
             rc = fail(FCONV_EHIP, "fconv_release: HIP error while freeing a workspace");
     }
     g_ws.clear();

@@ -25,6 +25,7 @@
 // for both operands (fp32: channels 4g..4g+3, one per MFMA step; bf16: channels
 // 8g..8g+7 in one step). A and B agree on the pairing, which is all that matters.
 #include <cstdint>
+#include <type_traits>
 
 #include "device_math.h"
 #include "internal.h"
@@ -92,43 +93,173 @@ __global__ void pack_weights(const typename Elem<BF16>::T* __restrict__ w,
     }
 }
 
-template <bool BF16>
-__device__ __forceinline__ u4 load_group(const typename Elem<BF16>::T* __restrict__ src,
-                                         long long plane, int nvalid) {
-    // Loads EPG consecutive channels (stride = plane) at one pixel; channels at or
-    // beyond nvalid read as zero.
-    if constexpr (!BF16) {
-        float v[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] = e < nvalid ? src[e * plane] : 0.0f;
-        u4 r;
-        r.x = __float_as_uint(v[0]); r.y = __float_as_uint(v[1]);
-        r.z = __float_as_uint(v[2]); r.w = __float_as_uint(v[3]);
-        return r;
-    } else {
-        unsigned int h[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) h[e] = e < nvalid ? (unsigned int)src[e * plane] : 0u;
-        u4 r;
-        r.x = h[0] | (h[1] << 16); r.y = h[2] | (h[3] << 16);
-        r.z = h[4] | (h[5] << 16); r.w = h[6] | (h[7] << 16);
-        return r;
-    }
+// ---------------------------------------------------------------------------------
+// Staging of one K chunk (CK input channels) into LDS, split into a global-load half
+// (into registers, issued before the previous chunk's MFMA work so the memory latency
+// overlaps it) and an LDS-store half. Trip counts are compile-time constants so all
+// of a thread's loads are in flight together.
+// ---------------------------------------------------------------------------------
+
+// All staging loads are raw buffer loads: the resource covers one image of x (or the
+// repacked weights), offsets are 32-bit, and an offset past the end (kOOB) reads as zero
+// without touching memory -- so padding channels, rows below the image and columns
+// right of it are zero-filled without branches around the loads.
+constexpr int kOOB = 0x7FFFFFF0;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, unsigned bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
 
-template <bool BF16, int ACT, bool POOL, class TL>
-__global__ __launch_bounds__(kThreads) void conv3x3_fused(
+// Halo tile, vector path (W a multiple of the 16-byte pixel group, 16-byte aligned x):
+// each item loads one 16-byte run of VW pixels from each of the EPG channels of one
+// channel group, then writes VW 16-byte LDS rows (one per pixel, channel-minor), i.e.
+// a small register transpose. Halo columns beyond TW+2 are loaded but not stored.
+template <bool BF16, class TL>
+struct HaloVec {
+    using T = typename Elem<BF16>::T;
+    static constexpr int ESZ = (int)sizeof(T);
+    static constexpr int EPG = Elem<BF16>::EPG;
+    static constexpr int VW = 16 / ESZ;                      // pixels per 16-byte load
+    static constexpr int NCG = (TL::HC + VW - 1) / VW;       // 16-byte column groups per row
+    static constexpr int ITEMS = TL::HR * NCG * 4;           // (row, column group, channel group)
+    static constexpr int PER = (ITEMS + kThreads - 1) / kThreads;
+    u4 v[PER][EPG];
+
+    __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t xr, int H, int W, int Cin, int c0, int oh0,
+                                         int ow0, int tid) {
+#pragma unroll
+        for (int j = 0; j < PER; ++j) {
+            const int it = tid + j * kThreads;
+            const int q = it & 3, cg = (it >> 2) % NCG, r = (it >> 2) / NCG;
+            const int ih = oh0 + r, iw = ow0 + cg * VW;
+            const bool inb = it < ITEMS && ih < H && iw < W;
+            const int base = ((c0 + q * EPG) * H + ih) * W + iw;
+#pragma unroll
+            for (int e = 0; e < EPG; ++e) {
+                const bool ok = inb && c0 + q * EPG + e < Cin;
+                v[j][e] = __builtin_amdgcn_raw_buffer_load_b128(xr, ok ? (base + e * H * W) * ESZ : kOOB, 0, 0);
+            }
+        }
+    }
+
+    __device__ __forceinline__ void store(unsigned char* halo, int tid) const {
+#pragma unroll
+        for (int j = 0; j < PER; ++j) {
+            const int it = tid + j * kThreads;
+            if (ITEMS % kThreads != 0 && it >= ITEMS) continue;
+            const int q = it & 3, cg = (it >> 2) % NCG, r = (it >> 2) / NCG;
+#pragma unroll
+            for (int p = 0; p < VW; ++p) {
+                const int col = cg * VW + p;
+                if (NCG * VW != TL::HC && col >= TL::HC) continue;
+                u4 o;
+                if constexpr (!BF16) {
+                    o = u4{v[j][0][p], v[j][1][p], v[j][2][p], v[j][3][p]};
+                } else {
+                    const int dw = p >> 1, sh = (p & 1) * 16;
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) {
+                        const unsigned lo = (v[j][2 * k][dw] >> sh) & 0xFFFFu;
+                        const unsigned hi = (v[j][2 * k + 1][dw] >> sh) & 0xFFFFu;
+                        o[k] = lo | (hi << 16);
+                    }
+                }
+                *(u4*)(halo + (r * TL::HC + col) * kRow + q * 16) = o;
+            }
+        }
+    }
+};
+
+// Halo tile, general path (any W, any alignment of x): element loads, one (position,
+// channel group) item at a time.
+template <bool BF16, class TL>
+struct HaloScalar {
+    using T = typename Elem<BF16>::T;
+    static constexpr int ESZ = (int)sizeof(T);
+    static constexpr int EPG = Elem<BF16>::EPG;
+    static constexpr int ITEMS = TL::HPOS * 4;
+    static constexpr int PER = (ITEMS + kThreads - 1) / kThreads;
+    u4 v[PER];
+
+    __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t xr, int H, int W, int Cin, int c0, int oh0,
+                                         int ow0, int tid) {
+#pragma unroll
+        for (int j = 0; j < PER; ++j) {
+            const int it = tid + j * kThreads;
+            const int q = it & 3, pos = it >> 2;
+            const int ih = oh0 + pos / TL::HC, iw = ow0 + pos % TL::HC;
+            const bool inb = it < ITEMS && ih < H && iw < W;
+            const int base = ((c0 + q * EPG) * H + ih) * W + iw;
+            unsigned h[EPG];
+#pragma unroll
+            for (int e = 0; e < EPG; ++e) {
+                const int off = (inb && c0 + q * EPG + e < Cin) ? (base + e * H * W) * ESZ : kOOB;
+                if constexpr (!BF16) h[e] = __builtin_amdgcn_raw_buffer_load_b32(xr, off, 0, 0);
+                else h[e] = __builtin_amdgcn_raw_buffer_load_b16(xr, off, 0, 0);
+            }
+            if constexpr (!BF16) v[j] = u4{h[0], h[1], h[2], h[3]};
+            else v[j] = u4{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16)};
+        }
+    }
+
+    __device__ __forceinline__ void store(unsigned char* halo, int tid) const {
+#pragma unroll
+        for (int j = 0; j < PER; ++j) {
+            const int it = tid + j * kThreads;
+            if (ITEMS % kThreads == 0 || it < ITEMS) *(u4*)(halo + (it >> 2) * kRow + (it & 3) * 16) = v[j];
+        }
+    }
+};
+
+// Weight slice of one chunk: 9 taps x BN output channels x 64 bytes, from the repacked
+// [chunk][tap][CoutPad][CK] layout (16-byte loads, contiguous per tap).
+template <bool BF16, class TL>
+struct WeightStage {
+    using T = typename Elem<BF16>::T;
+    static constexpr int ITEMS = 9 * TL::BN * 4;
+    static constexpr int PER = (ITEMS + kThreads - 1) / kThreads;
+    u4 v[PER];
+
+    __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t wr, int CoutPad, int ch, int oc0, int tid) {
+#pragma unroll
+        for (int j = 0; j < PER; ++j) {
+            const int it = tid + j * kThreads;
+            const int q = it & 3, row = it >> 2;
+            const int o = row % TL::BN, tap = row / TL::BN;
+            const int off = (((ch * 9 + tap) * CoutPad + oc0 + o) * 4 + q) * 16;
+            v[j] = __builtin_amdgcn_raw_buffer_load_b128(wr, (ITEMS % kThreads == 0 || it < ITEMS) ? off : kOOB, 0, 0);
+        }
+    }
+
+    __device__ __forceinline__ void store(unsigned char* wl, int tid) const {
+#pragma unroll
+        for (int j = 0; j < PER; ++j) {
+            const int it = tid + j * kThreads;
+            if (ITEMS % kThreads == 0 || it < ITEMS) *(u4*)(wl + (it >> 2) * kRow + (it & 3) * 16) = v[j];
+        }
+    }
+};
+
+// Workgroups are dispatched to the 8 XCDs round-robin by blockIdx.x; renumber them so
+// each XCD receives a contiguous range of logical tiles (neighbouring spatial tiles and
+// all oc tiles of a spatial tile share that XCD's L2).
+__device__ __forceinline__ int xcd_contiguous_index(int b, int G) {
+    const int xcd = b & 7, idx = b >> 3, per = G >> 3, rem = G & 7;
+    return xcd * per + (xcd < rem ? xcd : rem) + idx;
+}
+
+template <bool BF16, bool VEC, int ACT, bool POOL, class TL>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void conv3x3_fused(
     const typename Elem<BF16>::T* __restrict__ x, const typename Elem<BF16>::T* __restrict__ wp,
     const float* __restrict__ bias, float* __restrict__ dst, int Cin, int H, int W, int Cout,
     int CoutPad, int nChunk, int tilesH, int tilesW, int ocTiles, int out_align) {
     using T = typename Elem<BF16>::T;
     constexpr int CK = Elem<BF16>::CK;
-    constexpr int EPG = Elem<BF16>::EPG;
     __shared__ __attribute__((aligned(16))) unsigned char smem[TL::LDS];
     unsigned char* halo = smem;
     unsigned char* wl = smem + TL::HPOS * kRow;
 
-    int bid = blockIdx.x;
+    int bid = xcd_contiguous_index(blockIdx.x, gridDim.x);
     const int ot = bid % ocTiles; bid /= ocTiles;
     const int tw = bid % tilesW; bid /= tilesW;
     const int th = bid % tilesH;
@@ -147,30 +278,24 @@ __global__ __launch_bounds__(kThreads) void conv3x3_fused(
         for (int c = 0; c < TL::WOB; ++c) acc[a][c] = f4{0.f, 0.f, 0.f, 0.f};
 
     const long long plane = (long long)H * W;
-    const T* xn = x + (long long)n * Cin * plane;
+    const __amdgpu_buffer_rsrc_t xr = make_rsrc(x + (long long)n * Cin * plane, (unsigned)(Cin * plane * sizeof(T)));
+    const __amdgpu_buffer_rsrc_t wr = make_rsrc(wp, (unsigned)(nChunk * 9 * CoutPad * 64));
+
+    using Halo = typename std::conditional<VEC, HaloVec<BF16, TL>, HaloScalar<BF16, TL>>::type;
+    Halo hs;
+    WeightStage<BF16, TL> wsg;
+    hs.load(xr, H, W, Cin, 0, oh0, ow0, tid);
+    wsg.load(wr, CoutPad, 0, oc0, tid);
 
     for (int ch = 0; ch < nChunk; ++ch) {
-        if (ch) __syncthreads();
-        const int c0 = ch * CK;
-        // Halo tile: (TH+2) x (TW+2) positions, 4 channel groups each.
-        for (int it = tid; it < TL::HPOS * 4; it += kThreads) {
-            const int pos = it % TL::HPOS, q = it / TL::HPOS;
-            const int ih = oh0 + pos / TL::HC, iw = ow0 + pos % TL::HC;
-            const int cbase = c0 + q * EPG;
-            int nvalid = (ih < H && iw < W) ? Cin - cbase : 0;
-            const T* src = xn + (long long)cbase * plane + (long long)ih * W + iw;
-            u4 v = load_group<BF16>(src, plane, nvalid);
-            *(u4*)(halo + pos * kRow + q * 16) = v;
-        }
-        // Weight slice: 9 taps x BN oc x 64 bytes.
-        const T* wsrc = wp + ((long long)ch * 9 * CoutPad + oc0) * CK;
-        for (int it = tid; it < 9 * TL::BN * 4; it += kThreads) {
-            const int q = it & 3, r = it >> 2;
-            const int o = r % TL::BN, tap = r / TL::BN;
-            const u4* src = (const u4*)(wsrc + ((long long)tap * CoutPad + o) * CK) + q;
-            *(u4*)(wl + r * kRow + q * 16) = *src;
-        }
+        if (ch) __syncthreads();  // every wave is done reading the previous chunk
+        hs.store(halo, tid);
+        wsg.store(wl, tid);
         __syncthreads();
+        if (ch + 1 < nChunk) {    // next chunk's loads fly while this chunk computes
+            hs.load(xr, H, W, Cin, (ch + 1) * CK, oh0, ow0, tid);
+            wsg.load(wr, CoutPad, ch + 1, oc0, tid);
+        }
 
 #pragma unroll
         for (int tap = 0; tap < 9; ++tap) {
@@ -249,13 +374,13 @@ __global__ __launch_bounds__(kThreads) void conv3x3_fused(
                 red[wpi * TL::BN + (woi * TL::WOB + jo) * 16 + i] = psum[jo];
         }
         __syncthreads();
+        const int nTiles = tilesH * tilesW;
         if (tid < TL::BN) {
             float s = 0.0f;
 #pragma unroll
             for (int p = 0; p < TL::WP; ++p) s += red[p * TL::BN + tid];
             const int oc = oc0 + tid;
-            const int nTiles = tilesH * tilesW;
-            if (oc < Cout) dst[((long long)n * Cout + oc) * nTiles + th * tilesW + tw] = s;
+            if (oc < Cout) dst[((long long)n * nTiles + th * tilesW + tw) * Cout + oc] = s;
         }
     } else {
 #pragma unroll
@@ -289,26 +414,36 @@ __global__ __launch_bounds__(kThreads) void conv3x3_fused(
     }
 }
 
-// Sum of the per-tile partials of one (n, oc) map in a fixed order, divided by the
-// number of valid output positions. One wave per (n, oc).
-__global__ __launch_bounds__(256) void pool_finalize(const float* __restrict__ part,
-                                                     float* __restrict__ out, int NC, int nTiles,
-                                                     float area) {
-    const int wv = (int)(((long long)blockIdx.x * blockDim.x + threadIdx.x) >> 6);
-    const int lane = threadIdx.x & 63;
-    if (wv >= NC) return;
-    const float* p = part + (long long)wv * nTiles;
+// Pool level 2: out[n][oc] = (sum over tiles t of part[n][t][oc]) / area, summed in a
+// fixed order. One workgroup per (image, 64 output channels); its four waves take four
+// contiguous tile ranges (lanes = consecutive channels, so every load is one 256-byte
+// row), and the four range sums are added in range order through LDS.
+__global__ __launch_bounds__(256) void pool_finalize(const float* __restrict__ part, float* __restrict__ out,
+                                                     int Cout, int nTiles, float area) {
+    __shared__ float red[4][64];
+    const int n = blockIdx.x, lane = threadIdx.x & 63, sl = threadIdx.x >> 6;
+    const int oc = blockIdx.y * 64 + lane;
+    const int per = (nTiles + 3) / 4, t0 = sl * per, t1 = min(nTiles, t0 + per);
     float s = 0.0f;
-    for (int t = lane; t < nTiles; t += 64) s += p[t];
-    s = wave_sum(s);
-    if (lane == 0) out[wv] = s / area;
+    if (oc < Cout) {
+        const float* p = part + (long long)n * nTiles * Cout + oc;
+#pragma unroll 8
+        for (int t = t0; t < t1; ++t) s += p[(long long)t * Cout];
+    }
+    red[sl][lane] = s;
+    __syncthreads();
+    if (sl == 0 && oc < Cout) out[(long long)n * Cout + oc] = ((red[0][lane] + red[1][lane]) + red[2][lane] + red[3][lane]) / area;
 }
 
 template <bool BF16, int ACT, bool POOL, class TL>
 hipError_t launch_typed(const ConvPlan& p, const void* x, const void* wpk, const float* b,
                         float* dst, hipStream_t stream) {
     using T = typename Elem<BF16>::T;
-    hipLaunchKernelGGL((conv3x3_fused<BF16, ACT, POOL, TL>), dim3((unsigned)p.grid()), dim3(kThreads), 0,
+    // Vector halo loads need whole 16-byte pixel groups per row and an aligned base.
+    const int vw = 16 / (int)sizeof(T);
+    const bool vec = p.W % vw == 0 && (uintptr_t)x % 16 == 0;
+    auto kern = vec ? conv3x3_fused<BF16, true, ACT, POOL, TL> : conv3x3_fused<BF16, false, ACT, POOL, TL>;
+    hipLaunchKernelGGL(kern, dim3((unsigned)p.grid()), dim3(kThreads), 0,
                        stream, (const T*)x, (const T*)wpk, b, dst, p.Cin, p.H, p.W, p.Cout, p.CoutPad,
                        p.nChunk, p.tilesH, p.tilesW, p.ocTiles,
                        ((uintptr_t)dst % 16 == 0) ? 16 : ((uintptr_t)dst % 8 == 0 ? 8 : 4));
@@ -373,11 +508,9 @@ hipError_t launch_conv(const ConvPlan& p, const void* x, const void* w, const fl
                : launch_act<false, TileA>(p, x, wpk, b, dst, stream);
     if (timer) timer->end("conv3x3_fused", stream);
     if (e != hipSuccess || !p.pool) return e;
-    const int NC = p.N * p.Cout;
-    const unsigned fblocks = (unsigned)((NC + 3) / 4);
     if (timer) timer->begin("pool_finalize", stream);
-    hipLaunchKernelGGL(pool_finalize, dim3(fblocks), dim3(256), 0, stream, (const float*)part, out, NC,
-                       p.tilesH * p.tilesW, (float)((double)p.OH * (double)p.OW));
+    hipLaunchKernelGGL(pool_finalize, dim3((unsigned)p.N, (unsigned)((p.Cout + 63) / 64)), dim3(256), 0, stream,
+                       (const float*)part, out, p.Cout, p.tilesH * p.tilesW, (float)((double)p.OH * (double)p.OW));
     e = hipGetLastError();
     if (timer) timer->end("pool_finalize", stream);
     return e;

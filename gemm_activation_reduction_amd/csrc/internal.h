@@ -23,7 +23,7 @@ struct ConvPlan {
     int TH, TW, BN, CK;      // output tile rows/cols, oc per workgroup, channels per K chunk
     int tilesH, tilesW, ocTiles, nChunk, CoutPad;
     size_t wpack_bytes;      // repacked weights [nChunk][9][CoutPad][CK]
-    size_t part_bytes;       // pool partials [N][Cout][tilesH * tilesW] fp32
+    size_t part_bytes;       // pool partials [N][tilesH * tilesW][Cout] fp32
     size_t workspace_bytes() const { return wpack_bytes + part_bytes; }
     long long grid() const { return (long long)N * tilesH * tilesW * ocTiles; }
 };

@@ -162,3 +162,15 @@ def test_conv_full_size_mish2_full_output_sampled():
     err = max_rel_err(got, ref)
     print(f"{name}: sampled err={err:.3e}", flush=True)
     assert err <= TOL_F32
+
+
+def test_conv_pool_repeated_calls_with_changing_shapes():
+    # The pooled path keeps per-image completion counters in the library's workspace;
+    # every call must leave them ready for the next one, whatever its shape.
+    cases = [(4, 16, 40, 36, 64), (2, 3, 17, 19, 8), (6, 20, 12, 70, 40), (4, 16, 40, 36, 64)]
+    for k, shape in enumerate(cases * 2):
+        bf16 = k % 3 == 1
+        x, w, b = rand_case(50 + k % len(cases), *shape, bf16=bf16)
+        got = run_conv(x, w, b, fc.ACT_GELU, 1, bf16)
+        ref = oracle.conv_act_pool(x, w, b, fc.ACT_GELU, 1)
+        assert max_rel_err(got, ref) <= (TOL_BF16 if bf16 else TOL_F32), (k, shape)
