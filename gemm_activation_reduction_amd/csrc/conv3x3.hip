@@ -52,23 +52,33 @@ template <> struct Elem<true> {
     static constexpr int EPG = 8;
 };
 
-template <int TH_, int TW_, int BN_, int WP_, int WO_>
+template <int TH_, int TW_, int BN_, int WP_, int WO_, int MINW_, int PFD_, int NT_>
 struct Tile {
     static constexpr int TH = TH_, TW = TW_, BN = BN_, WP = WP_, WO = WO_;
+    static constexpr int NT = NT_;              // threads per workgroup (NT / 64 waves)
+    static constexpr int MINW = MINW_;          // waves per SIMD the register budget targets
+    static constexpr int PFD = PFD_;            // halo prefetch depth in K chunks (1 or 2)
     static constexpr int CB = TW / 16;          // 16-pixel blocks per tile row
     static constexpr int PB = TH * CB;          // pixel blocks per tile
     static constexpr int OB = BN / 16;          // oc blocks per tile
     static constexpr int WPB = PB / WP;         // pixel blocks per wave
     static constexpr int WOB = OB / WO;         // oc blocks per wave
-    static constexpr int HR = TH + 2, HC = TW + 2, HPOS = HR * HC;
+    static constexpr int HR = TH + 2, HC = TW + 2;
+    // Halo row pitch in positions: HP = 4 (mod 8) makes the staging stores of two
+    // neighbouring halo rows land on disjoint LDS banks.
+    static constexpr int HP = HC + ((4 - HC % 8) + 8) % 8, HPOS = HR * HP;
     static constexpr int LDS = HPOS * kRow + 9 * BN * kRow;
-    static_assert(WP * WO == kThreads / 64, "four waves");
+    static_assert(WP * WO == NT / 64, "one wave per (pixel group, oc group)");
     static_assert(PB % WP == 0 && OB % WO == 0, "even wave split");
     static_assert(TW % 16 == 0 && BN % 16 == 0, "MFMA block multiples");
 };
 
 // Tile configurations (index = ConvPlan::tile_cfg).
-using TileA = Tile<8, 32, 64, 4, 1>;   // 256 pixels x 64 oc; wave = 4 pixel blocks x 4 oc blocks
+// fp32: 256 pixels x 64 oc; wave = 4 pixel blocks x 4 oc blocks; 2 workgroups per CU.
+using TileA = Tile<8, 32, 64, 4, 1, 2, 1, 256>;
+// bf16: the same tile shape (measured on MI355X: a 256 x 128 tile with 8 waves and one
+// workgroup per CU, or 32-oc tiles with 3 workgroups per CU, were both slower).
+using TileB = Tile<8, 32, 64, 4, 1, 2, 1, 256>;
 
 // Repack OIHW weights to [chunk][tap][CoutPad][CK], zero-filling channels >= Cin and
 // oc >= Cout, so a workgroup's slice for one chunk is 9 contiguous [BN][CK] blocks.
@@ -122,15 +132,33 @@ struct HaloVec {
     static constexpr int VW = 16 / ESZ;                      // pixels per 16-byte load
     static constexpr int NCG = (TL::HC + VW - 1) / VW;       // 16-byte column groups per row
     static constexpr int ITEMS = TL::HR * NCG * 4;           // (row, column group, channel group)
-    static constexpr int PER = (ITEMS + kThreads - 1) / kThreads;
+    static constexpr int PER = (ITEMS + TL::NT - 1) / TL::NT;
     u4 v[PER][EPG];
+
+    // Item -> (channel group q, column group cg, halo row r). The LDS stores of a
+    // wave are processed eight lanes at a time; each group of eight must cover eight
+    // distinct 16-byte bank slots. fp32 (4-pixel runs): 4 channel groups x 2 adjacent
+    // column groups. bf16 (8-pixel runs, where adjacent column groups share banks):
+    // 4 channel groups x 2 adjacent rows, which the halo pitch HP = 4 (mod 8) separates.
+    __device__ __forceinline__ static void item(int it, int& q, int& cg, int& r) {
+        q = it & 3;
+        if constexpr (!BF16) {
+            cg = (it >> 2) % NCG;
+            r = (it >> 2) / NCG;
+        } else {
+            static_assert(TL::HR % 2 == 0, "bf16 staging pairs halo rows");
+            cg = (it >> 3) % NCG;
+            r = 2 * ((it >> 3) / NCG) + ((it >> 2) & 1);
+        }
+    }
 
     __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t xr, int H, int W, int Cin, int c0, int oh0,
                                          int ow0, int tid) {
 #pragma unroll
         for (int j = 0; j < PER; ++j) {
-            const int it = tid + j * kThreads;
-            const int q = it & 3, cg = (it >> 2) % NCG, r = (it >> 2) / NCG;
+            const int it = tid + j * TL::NT;
+            int q, cg, r;
+            item(it, q, cg, r);
             const int ih = oh0 + r, iw = ow0 + cg * VW;
             const bool inb = it < ITEMS && ih < H && iw < W;
             const int base = ((c0 + q * EPG) * H + ih) * W + iw;
@@ -145,13 +173,14 @@ struct HaloVec {
     __device__ __forceinline__ void store(unsigned char* halo, int tid) const {
 #pragma unroll
         for (int j = 0; j < PER; ++j) {
-            const int it = tid + j * kThreads;
-            if (ITEMS % kThreads != 0 && it >= ITEMS) continue;
-            const int q = it & 3, cg = (it >> 2) % NCG, r = (it >> 2) / NCG;
+            const int it = tid + j * TL::NT;
+            if (ITEMS % TL::NT != 0 && it >= ITEMS) continue;
+            int q, cg, r;
+            item(it, q, cg, r);
 #pragma unroll
             for (int p = 0; p < VW; ++p) {
                 const int col = cg * VW + p;
-                if (NCG * VW != TL::HC && col >= TL::HC) continue;
+                if (NCG * VW > TL::HP && col >= TL::HP) continue;
                 u4 o;
                 if constexpr (!BF16) {
                     o = u4{v[j][0][p], v[j][1][p], v[j][2][p], v[j][3][p]};
@@ -164,7 +193,7 @@ struct HaloVec {
                         o[k] = lo | (hi << 16);
                     }
                 }
-                *(u4*)(halo + (r * TL::HC + col) * kRow + q * 16) = o;
+                *(u4*)(halo + (r * TL::HP + col) * kRow + q * 16) = o;
             }
         }
     }
@@ -177,15 +206,15 @@ struct HaloScalar {
     using T = typename Elem<BF16>::T;
     static constexpr int ESZ = (int)sizeof(T);
     static constexpr int EPG = Elem<BF16>::EPG;
-    static constexpr int ITEMS = TL::HPOS * 4;
-    static constexpr int PER = (ITEMS + kThreads - 1) / kThreads;
+    static constexpr int ITEMS = TL::HR * TL::HC * 4;
+    static constexpr int PER = (ITEMS + TL::NT - 1) / TL::NT;
     u4 v[PER];
 
     __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t xr, int H, int W, int Cin, int c0, int oh0,
                                          int ow0, int tid) {
 #pragma unroll
         for (int j = 0; j < PER; ++j) {
-            const int it = tid + j * kThreads;
+            const int it = tid + j * TL::NT;
             const int q = it & 3, pos = it >> 2;
             const int ih = oh0 + pos / TL::HC, iw = ow0 + pos % TL::HC;
             const bool inb = it < ITEMS && ih < H && iw < W;
@@ -205,8 +234,10 @@ struct HaloScalar {
     __device__ __forceinline__ void store(unsigned char* halo, int tid) const {
 #pragma unroll
         for (int j = 0; j < PER; ++j) {
-            const int it = tid + j * kThreads;
-            if (ITEMS % kThreads == 0 || it < ITEMS) *(u4*)(halo + (it >> 2) * kRow + (it & 3) * 16) = v[j];
+            const int it = tid + j * TL::NT;
+            const int pos = it >> 2;
+            if (ITEMS % TL::NT == 0 || it < ITEMS)
+                *(u4*)(halo + ((pos / TL::HC) * TL::HP + pos % TL::HC) * kRow + (it & 3) * 16) = v[j];
         }
     }
 };
@@ -216,26 +247,28 @@ struct HaloScalar {
 template <bool BF16, class TL>
 struct WeightStage {
     using T = typename Elem<BF16>::T;
-    static constexpr int ITEMS = 9 * TL::BN * 4;
-    static constexpr int PER = (ITEMS + kThreads - 1) / kThreads;
+    static constexpr int ITEMS = 9 * TL::BN * 4;   // (16 rows x 4 groups) per 64 items
+    static constexpr int PER = (ITEMS + TL::NT - 1) / TL::NT;
+    static_assert(ITEMS % 64 == 0, "BN multiple of 16");
     u4 v[PER];
 
     __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t wr, int CoutPad, int ch, int oc0, int tid) {
 #pragma unroll
         for (int j = 0; j < PER; ++j) {
-            const int it = tid + j * kThreads;
-            const int q = it & 3, row = it >> 2;
+            const int it = tid + j * TL::NT;
+            const int q = (it >> 4) & 3, row = (it & 15) + 16 * (it >> 6);
             const int o = row % TL::BN, tap = row / TL::BN;
             const int off = (((ch * 9 + tap) * CoutPad + oc0 + o) * 4 + q) * 16;
-            v[j] = __builtin_amdgcn_raw_buffer_load_b128(wr, (ITEMS % kThreads == 0 || it < ITEMS) ? off : kOOB, 0, 0);
+            v[j] = __builtin_amdgcn_raw_buffer_load_b128(wr, (ITEMS % TL::NT == 0 || it < ITEMS) ? off : kOOB, 0, 0);
         }
     }
 
     __device__ __forceinline__ void store(unsigned char* wl, int tid) const {
 #pragma unroll
         for (int j = 0; j < PER; ++j) {
-            const int it = tid + j * kThreads;
-            if (ITEMS % kThreads == 0 || it < ITEMS) *(u4*)(wl + (it >> 2) * kRow + (it & 3) * 16) = v[j];
+            const int it = tid + j * TL::NT;
+            const int q = (it >> 4) & 3, row = (it & 15) + 16 * (it >> 6);
+            if (ITEMS % TL::NT == 0 || it < ITEMS) *(u4*)(wl + row * kRow + q * 16) = v[j];
         }
     }
 };
@@ -249,7 +282,7 @@ __device__ __forceinline__ int xcd_contiguous_index(int b, int G) {
 }
 
 template <bool BF16, bool VEC, int ACT, bool POOL, class TL>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void conv3x3_fused(
+__global__ __launch_bounds__(TL::NT) __attribute__((amdgpu_waves_per_eu(TL::MINW))) void conv3x3_fused(
     const typename Elem<BF16>::T* __restrict__ x, const typename Elem<BF16>::T* __restrict__ wp,
     const float* __restrict__ bias, float* __restrict__ dst, int Cin, int H, int W, int Cout,
     int CoutPad, int nChunk, int tilesH, int tilesW, int ocTiles, int out_align) {
@@ -270,6 +303,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int g = lane >> 4, i = lane & 15;
     const int wpi = wave % TL::WP, woi = wave / TL::WP;
+    // Pixel block pb -> (tile row, 16-column block). fp32 enumerates rows first, so a
+    // wave's blocks are one column of rows and A fragments repeat across kh taps (fewer
+    // LDS reads); bf16 uses 2 x 2 blocks, which needs fewer live registers.
+    auto pb_row = [](int pb) { return BF16 ? pb / TL::CB : pb % TL::TH; };
+    auto pb_col = [](int pb) { return BF16 ? pb % TL::CB : pb / TL::TH; };
 
     f4 acc[TL::WPB][TL::WOB];
 #pragma unroll
@@ -281,60 +319,90 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     const __amdgpu_buffer_rsrc_t xr = make_rsrc(x + (long long)n * Cin * plane, (unsigned)(Cin * plane * sizeof(T)));
     const __amdgpu_buffer_rsrc_t wr = make_rsrc(wp, (unsigned)(nChunk * 9 * CoutPad * 64));
 
-    using Halo = typename std::conditional<VEC, HaloVec<BF16, TL>, HaloScalar<BF16, TL>>::type;
-    Halo hs;
-    WeightStage<BF16, TL> wsg;
-    hs.load(xr, H, W, Cin, 0, oh0, ow0, tid);
-    wsg.load(wr, CoutPad, 0, oc0, tid);
-
-    for (int ch = 0; ch < nChunk; ++ch) {
-        if (ch) __syncthreads();  // every wave is done reading the previous chunk
-        hs.store(halo, tid);
-        wsg.store(wl, tid);
-        __syncthreads();
-        if (ch + 1 < nChunk) {    // next chunk's loads fly while this chunk computes
-            hs.load(xr, H, W, Cin, (ch + 1) * CK, oh0, ow0, tid);
-            wsg.load(wr, CoutPad, ch + 1, oc0, tid);
-        }
-
-#pragma unroll
+    // Nine shifted tap GEMMs over the chunk held in LDS.
+    auto compute_chunk = [&]() {
+    #pragma unroll
         for (int tap = 0; tap < 9; ++tap) {
             const int kh = tap / 3, kw = tap % 3;
             u4 a[TL::WPB], b[TL::WOB];
-#pragma unroll
+    #pragma unroll
             for (int j = 0; j < TL::WPB; ++j) {
                 const int pb = wpi * TL::WPB + j;
-                const int pos = (pb / TL::CB + kh) * TL::HC + (pb % TL::CB) * 16 + i + kw;
+                const int pos = (pb_row(pb) + kh) * TL::HP + pb_col(pb) * 16 + i + kw;
                 a[j] = *(const u4*)(halo + pos * kRow + g * 16);
             }
-#pragma unroll
+    #pragma unroll
             for (int j = 0; j < TL::WOB; ++j) {
                 const int o = (woi * TL::WOB + j) * 16 + i;
                 b[j] = *(const u4*)(wl + (tap * TL::BN + o) * kRow + g * 16);
             }
             if constexpr (!BF16) {
-#pragma unroll
+    #pragma unroll
                 for (int s = 0; s < 4; ++s)
-#pragma unroll
+    #pragma unroll
                     for (int jp = 0; jp < TL::WPB; ++jp)
-#pragma unroll
+    #pragma unroll
                         for (int jo = 0; jo < TL::WOB; ++jo)
                             acc[jp][jo] = __builtin_amdgcn_mfma_f32_16x16x4f32(
                                 __uint_as_float(a[jp][s]), __uint_as_float(b[jo][s]), acc[jp][jo], 0, 0, 0);
             } else {
-#pragma unroll
+    #pragma unroll
                 for (int jp = 0; jp < TL::WPB; ++jp)
-#pragma unroll
+    #pragma unroll
                     for (int jo = 0; jo < TL::WOB; ++jo)
                         acc[jp][jo] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
                             __builtin_bit_cast(bf16x8, a[jp]), __builtin_bit_cast(bf16x8, b[jo]),
                             acc[jp][jo], 0, 0, 0);
             }
         }
+    };
+
+    using Halo = typename std::conditional<VEC, HaloVec<BF16, TL>, HaloScalar<BF16, TL>>::type;
+    WeightStage<BF16, TL> wsg;
+    if constexpr (TL::PFD == 1) {
+        // One chunk ahead: the next chunk's loads fly while this chunk computes.
+        Halo hs;
+        hs.load(xr, H, W, Cin, 0, oh0, ow0, tid);
+        wsg.load(wr, CoutPad, 0, oc0, tid);
+        for (int ch = 0; ch < nChunk; ++ch) {
+            if (ch) __syncthreads();  // every wave is done reading the previous chunk
+            hs.store(halo, tid);
+            wsg.store(wl, tid);
+            __syncthreads();
+            if (ch + 1 < nChunk) {
+                hs.load(xr, H, W, Cin, (ch + 1) * CK, oh0, ow0, tid);
+                wsg.load(wr, CoutPad, ch + 1, oc0, tid);
+            }
+            compute_chunk();
+        }
+    } else {
+        // Halo tiles two chunks ahead (two register sets, alternating), weights one ahead.
+        Halo h0, h1;
+        h0.load(xr, H, W, Cin, 0, oh0, ow0, tid);
+        wsg.load(wr, CoutPad, 0, oc0, tid);
+        if (nChunk > 1) h1.load(xr, H, W, Cin, CK, oh0, ow0, tid);
+        for (int ch = 0; ch < nChunk; ch += 2) {
+            if (ch) __syncthreads();
+            h0.store(halo, tid);
+            wsg.store(wl, tid);
+            __syncthreads();
+            if (ch + 2 < nChunk) h0.load(xr, H, W, Cin, (ch + 2) * CK, oh0, ow0, tid);
+            if (ch + 1 < nChunk) wsg.load(wr, CoutPad, ch + 1, oc0, tid);
+            compute_chunk();
+            if (ch + 1 >= nChunk) break;
+            __syncthreads();
+            h1.store(halo, tid);
+            wsg.store(wl, tid);
+            __syncthreads();
+            if (ch + 3 < nChunk) h1.load(xr, H, W, Cin, (ch + 3) * CK, oh0, ow0, tid);
+            if (ch + 2 < nChunk) wsg.load(wr, CoutPad, ch + 2, oc0, tid);
+            compute_chunk();
+        }
     }
 
     // Epilogue. Accumulator layout (16x16 MFMA output): lane (g, i) register r holds
     // pixel 4g + r of the pixel block and output channel i of the oc block.
+    const bool interior = oh0 + TL::TH <= OH && ow0 + TL::TW <= OW;  // uniform per workgroup
     float bv[TL::WOB];
 #pragma unroll
     for (int j = 0; j < TL::WOB; ++j) {
@@ -349,11 +417,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
 #pragma unroll
         for (int jp = 0; jp < TL::WPB; ++jp) {
             const int pb = wpi * TL::WPB + jp;
-            const int oh = oh0 + pb / TL::CB;
-            const int owb = ow0 + (pb % TL::CB) * 16 + 4 * g;
+            const int oh = oh0 + pb_row(pb);
+            const int owb = ow0 + pb_col(pb) * 16 + 4 * g;
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const bool valid = oh < OH && owb + r < OW;
+                const bool valid = interior || (oh < OH && owb + r < OW);
 #pragma unroll
                 for (int jo = 0; jo < TL::WOB; ++jo) {
                     const float v = activate<ACT>(acc[jp][jo][r] + bv[jo]);
@@ -386,8 +454,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
 #pragma unroll
         for (int jp = 0; jp < TL::WPB; ++jp) {
             const int pb = wpi * TL::WPB + jp;
-            const int oh = oh0 + pb / TL::CB;
-            const int owb = ow0 + (pb % TL::CB) * 16 + 4 * g;
+            const int oh = oh0 + pb_row(pb);
+            const int owb = ow0 + pb_col(pb) * 16 + 4 * g;
             if (oh >= OH) continue;
 #pragma unroll
             for (int jo = 0; jo < TL::WOB; ++jo) {
@@ -443,7 +511,7 @@ hipError_t launch_typed(const ConvPlan& p, const void* x, const void* wpk, const
     const int vw = 16 / (int)sizeof(T);
     const bool vec = p.W % vw == 0 && (uintptr_t)x % 16 == 0;
     auto kern = vec ? conv3x3_fused<BF16, true, ACT, POOL, TL> : conv3x3_fused<BF16, false, ACT, POOL, TL>;
-    hipLaunchKernelGGL(kern, dim3((unsigned)p.grid()), dim3(kThreads), 0,
+    hipLaunchKernelGGL(kern, dim3((unsigned)p.grid()), dim3(TL::NT), 0,
                        stream, (const T*)x, (const T*)wpk, b, dst, p.Cin, p.H, p.W, p.Cout, p.CoutPad,
                        p.nChunk, p.tilesH, p.tilesW, p.ocTiles,
                        ((uintptr_t)dst % 16 == 0) ? 16 : ((uintptr_t)dst % 8 == 0 ? 8 : 4));
@@ -472,7 +540,10 @@ ConvPlan plan_conv(bool bf16, int act, int pool, int N, int Cin, int H, int W, i
     p.N = N; p.Cin = Cin; p.H = H; p.W = W; p.Cout = Cout;
     p.OH = H - 2; p.OW = W - 2;
     p.tile_cfg = 0;
-    p.TH = TileA::TH; p.TW = TileA::TW; p.BN = TileA::BN;
+    p.tile_cfg = bf16 ? 1 : 0;
+    p.TH = bf16 ? TileB::TH : TileA::TH;
+    p.TW = bf16 ? TileB::TW : TileA::TW;
+    p.BN = bf16 ? TileB::BN : TileA::BN;
     p.CK = bf16 ? Elem<true>::CK : Elem<false>::CK;
     p.tilesH = (p.OH + p.TH - 1) / p.TH;
     p.tilesW = (p.OW + p.TW - 1) / p.TW;
@@ -504,7 +575,7 @@ hipError_t launch_conv(const ConvPlan& p, const void* x, const void* w, const fl
     if (e != hipSuccess) return e;
     float* dst = p.pool ? part : out;
     if (timer) timer->begin("conv3x3_fused", stream);
-    e = p.bf16 ? launch_act<true, TileA>(p, x, wpk, b, dst, stream)
+    e = p.bf16 ? launch_act<true, TileB>(p, x, wpk, b, dst, stream)
                : launch_act<false, TileA>(p, x, wpk, b, dst, stream);
     if (timer) timer->end("conv3x3_fused", stream);
     if (e != hipSuccess || !p.pool) return e;

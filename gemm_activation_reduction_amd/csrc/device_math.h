@@ -13,33 +13,35 @@ __device__ __forceinline__ float fast_exp(float v) {
     return __builtin_amdgcn_exp2f(v * 1.4426950408889634f);
 }
 
-// Exact-form GELU, 0.5 v (1 + erf(v / sqrt 2)) ("Kimi-K2.6 l2_p67" page: PyTorch's
-// default approximate='none' form, not the tanh approximation).
-// erf is evaluated with the rational approximation of Abramowitz & Stegun,
-// Handbook of Mathematical Functions, formula 7.1.26 (Hastings):
+// Exact-form GELU, 0.5 v (1 + erf(v / sqrt 2)) = v Phi(v) ("Kimi-K2.6 l2_p67" page:
+// PyTorch's default approximate='none' form, not the tanh approximation).
+// erfc is evaluated with the rational approximation of Abramowitz & Stegun, Handbook of
+// Mathematical Functions, formula 7.1.26 (Hastings):
 //   erfc(u) = t (a1 + t (a2 + t (a3 + t (a4 + t a5)))) e^{-u^2},  t = 1 / (1 + p u),  u >= 0,
-// with |error| <= 1.5e-7. For v < 0 the result is formed as 0.5 v erfc(|v| / sqrt 2),
-// so the negative tail keeps its absolute accuracy instead of cancelling 1 - erf.
+// |error| <= 1.5e-7. With u = |v| / sqrt 2 and h = erfc(u) / 2 (the coefficients below are
+// a_k / 2 and p / sqrt 2), v Phi(v) = max(v, 0) - |v| h for either sign of v, because
+// Phi(v) = 1 - h for v >= 0 and h for v < 0. The negative tail keeps its absolute
+// accuracy (no 1 - erf cancellation). 11 VALU operations and two transcendentals.
 __device__ __forceinline__ float gelu_erf(float v) {
-    const float u = fabsf(v) * 0.70710678118654752f;
-    const float t = __builtin_amdgcn_rcpf(fmaf(0.3275911f, u, 1.0f));
-    float poly = fmaf(t, 1.061405429f, -1.453152027f);
-    poly = fmaf(t, poly, 1.421413741f);
-    poly = fmaf(t, poly, -0.284496736f);
-    poly = fmaf(t, poly, 0.254829592f);
-    const float erfc_u = t * poly * fast_exp(-u * u);
-    return 0.5f * v * (v >= 0.0f ? 2.0f - erfc_u : erfc_u);
+    const float av = fabsf(v);
+    const float t = __builtin_amdgcn_rcpf(fmaf(0.23164189952630458f, av, 1.0f));  // 0.3275911 / sqrt 2
+    float p = fmaf(t, 0.5307027145f, -0.7265760135f);
+    p = fmaf(t, p, 0.7107068705f);
+    p = fmaf(t, p, -0.142248368f);
+    p = fmaf(t, p, 0.127414796f);
+    const float e = __builtin_amdgcn_exp2f(v * (v * -0.72134752044448170f));  // e^{-v^2/2}
+    const float h = (t * p) * e;
+    return fmaf(-av, h, fmaxf(v, 0.0f));
 }
 
-// Mish(v) = v tanh(softplus(v)). With t = e^v, tanh(log(1 + t)) = (t^2 + 2t) / (t^2 + 2t + 2),
-// so mish(v) = v * q / (q + 2) with q = t (t + 2): one exponential and one reciprocal.
-// For v > 20 the ratio is 1 to fp32 precision (2 / (q + 2) < 1e-17), so v is returned;
-// for very negative v, q underflows to 0 and mish(v) -> 0 as the exact function does.
+// Mish(v) = v tanh(softplus(v)). With t = e^v, tanh(log(1 + t)) = q / (q + 2), q = t (t + 2):
+// one exponential and one reciprocal. t is taken at min(v, 20): for v > 20 the ratio is 1
+// to fp32 precision (2 / (q + 2) < 1e-17), so the result is v; for very negative v, q
+// underflows to 0 and mish(v) -> 0 as the exact function does.
 __device__ __forceinline__ float mish_f32(float v) {
-    float t = fast_exp(fminf(v, 20.0f));
-    float q = t * (t + 2.0f);
-    float r = q * __builtin_amdgcn_rcpf(q + 2.0f);
-    return v > 20.0f ? v : v * r;
+    const float t = fast_exp(fminf(v, 20.0f));
+    const float q = t * (t + 2.0f);
+    return v * (q * __builtin_amdgcn_rcpf(q + 2.0f));
 }
 
 template <int ACT>

@@ -76,28 +76,32 @@ __global__ __launch_bounds__(kThreads) void gemm_lse_partials(
         for (int b = 0; b < TL::NB; ++b) acc[a][b] = f4{0.f, 0.f, 0.f, 0.f};
 
     f4 ra[TL::LA], rb[TL::LB];
+    // Item it -> (row, 16-byte K group): each 64 items are 16 rows x 4 groups, so the
+    // LDS stores of eight consecutive lanes hit eight distinct bank slots.
+    auto row_of = [](int it) { return (it & 15) + 16 * (it >> 6); };
+    auto grp_of = [](int it) { return (it >> 4) & 3; };
     auto gload = [&](int k0) {
 #pragma unroll
         for (int j = 0; j < TL::LA; ++j) {
             const int it = tid + j * kThreads;
-            ra[j] = load4<VEC>(X, M, K, m0 + (it >> 2), k0 + (it & 3) * 4);
+            ra[j] = load4<VEC>(X, M, K, m0 + row_of(it), k0 + grp_of(it) * 4);
         }
 #pragma unroll
         for (int j = 0; j < TL::LB; ++j) {
             const int it = tid + j * kThreads;
-            rb[j] = load4<VEC>(Wt, N, K, n0 + (it >> 2), k0 + (it & 3) * 4);
+            rb[j] = load4<VEC>(Wt, N, K, n0 + row_of(it), k0 + grp_of(it) * 4);
         }
     };
     auto sstore = [&](int buf) {
 #pragma unroll
         for (int j = 0; j < TL::LA; ++j) {
             const int it = tid + j * kThreads;
-            *(f4*)&As[buf][(it >> 2) * kPitch + (it & 3) * 4] = ra[j];
+            *(f4*)&As[buf][row_of(it) * kPitch + grp_of(it) * 4] = ra[j];
         }
 #pragma unroll
         for (int j = 0; j < TL::LB; ++j) {
             const int it = tid + j * kThreads;
-            *(f4*)&Bs[buf][(it >> 2) * kPitch + (it & 3) * 4] = rb[j];
+            *(f4*)&Bs[buf][row_of(it) * kPitch + grp_of(it) * 4] = rb[j];
         }
     };
 
