@@ -10,8 +10,8 @@
 //   kernel 2 (lse_merge_mish): one wave per row merges the pairs with the page's
 //     online logsumexp rule, M = max m_t, S = sum s_t e^(m_t - M), in a fixed
 //     order, then writes z * mish(z) with z = M + log S.
-// Both operands are K-contiguous (x [M][K], w [N][K]); LDS rows are 16 floats of
-// K plus 4 floats of padding (20-dword pitch: conflict-free 16-byte fragment reads).
+// Both operands are K-contiguous (x [M][K], w [N][K]); LDS rows are BK floats of
+// K plus 4 floats of padding (conflict-free 16-byte fragment reads).
 #include "device_math.h"
 #include "internal.h"
 
@@ -20,22 +20,23 @@ namespace {
 
 typedef float f4 __attribute__((ext_vector_type(4)));
 
-constexpr int kThreads = 256;
-constexpr int BK = 16;
-constexpr int kPitch = 20;  // floats per LDS row
-
-template <int BM_, int BN_, int WM_, int WN_>
+template <int BM_, int BN_, int WM_, int WN_, int BK_, int NT_>
 struct GTile {
     static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_;
+    static constexpr int NT = NT_;             // threads per workgroup
+    static constexpr int BK = BK_;             // K per LDS stage (multiple of 16)
+    static constexpr int KG = BK / 4;          // 16-byte K groups per row
+    static constexpr int PITCH = BK + 4;       // floats per LDS row (4 floats of padding)
     static constexpr int MB = BM / WM / 16;   // 16-row blocks per wave
     static constexpr int NB = BN / WN / 16;   // 16-col blocks per wave
-    static constexpr int LA = BM * BK / 4 / kThreads;  // float4 loads per thread (A)
-    static constexpr int LB = BN * BK / 4 / kThreads;  // float4 loads per thread (B)
-    static_assert(WM * WN == kThreads / 64, "four waves");
-    static_assert(LA >= 1 && LB >= 1, "tile too small for the loader");
+    static constexpr int IA = BM * KG, IB = BN * KG;  // float4 items per stage
+    static constexpr int LA = (IA + NT - 1) / NT;      // float4 loads per thread (A)
+    static constexpr int LB = (IB + NT - 1) / NT;      // float4 loads per thread (B)
+    static_assert(WM * WN == NT / 64, "one wave per (row group, column group)");
 };
 
-using GTileA = GTile<128, 128, 2, 2>;
+// 256 x 192 tiles: 2048 x 6144 is exactly 256 tiles, one per CU; 8 waves of 64 x 96.
+using GTileA = GTile<256, 192, 4, 2, 16, 512>;
 
 template <bool VEC>
 __device__ __forceinline__ f4 load4(const float* __restrict__ base, int rows, int K, int row, int k) {
@@ -56,9 +57,10 @@ __device__ __forceinline__ f4 load4(const float* __restrict__ base, int rows, in
 }
 
 template <class TL, bool VEC>
-__global__ __launch_bounds__(kThreads) void gemm_lse_partials(
+__global__ __launch_bounds__(TL::NT) void gemm_lse_partials(
     const float* __restrict__ X, const float* __restrict__ Wt, const float* __restrict__ bias,
     float2* __restrict__ part, int M, int K, int N, float scale, float cmin, float cmax, int tilesN) {
+    constexpr int BK = TL::BK, kPitch = TL::PITCH;
     __shared__ __attribute__((aligned(16))) float As[2][TL::BM * kPitch];
     __shared__ __attribute__((aligned(16))) float Bs[2][TL::BN * kPitch];
 
@@ -76,32 +78,32 @@ __global__ __launch_bounds__(kThreads) void gemm_lse_partials(
         for (int b = 0; b < TL::NB; ++b) acc[a][b] = f4{0.f, 0.f, 0.f, 0.f};
 
     f4 ra[TL::LA], rb[TL::LB];
-    // Item it -> (row, 16-byte K group): each 64 items are 16 rows x 4 groups, so the
-    // LDS stores of eight consecutive lanes hit eight distinct bank slots.
-    auto row_of = [](int it) { return (it & 15) + 16 * (it >> 6); };
-    auto grp_of = [](int it) { return (it >> 4) & 3; };
+    // Item it -> (row, 16-byte K group): each 16 * KG items are 16 rows x KG groups with
+    // rows fastest, so the LDS stores of eight consecutive lanes hit distinct bank slots.
+    auto row_of = [](int it) { return (it & 15) + 16 * (it / (16 * TL::KG)); };
+    auto grp_of = [](int it) { return (it >> 4) % TL::KG; };
     auto gload = [&](int k0) {
 #pragma unroll
         for (int j = 0; j < TL::LA; ++j) {
-            const int it = tid + j * kThreads;
-            ra[j] = load4<VEC>(X, M, K, m0 + row_of(it), k0 + grp_of(it) * 4);
+            const int it = tid + j * TL::NT;
+            if (TL::IA % TL::NT == 0 || it < TL::IA) ra[j] = load4<VEC>(X, M, K, m0 + row_of(it), k0 + grp_of(it) * 4);
         }
 #pragma unroll
         for (int j = 0; j < TL::LB; ++j) {
-            const int it = tid + j * kThreads;
-            rb[j] = load4<VEC>(Wt, N, K, n0 + row_of(it), k0 + grp_of(it) * 4);
+            const int it = tid + j * TL::NT;
+            if (TL::IB % TL::NT == 0 || it < TL::IB) rb[j] = load4<VEC>(Wt, N, K, n0 + row_of(it), k0 + grp_of(it) * 4);
         }
     };
     auto sstore = [&](int buf) {
 #pragma unroll
         for (int j = 0; j < TL::LA; ++j) {
-            const int it = tid + j * kThreads;
-            *(f4*)&As[buf][row_of(it) * kPitch + grp_of(it) * 4] = ra[j];
+            const int it = tid + j * TL::NT;
+            if (TL::IA % TL::NT == 0 || it < TL::IA) *(f4*)&As[buf][row_of(it) * kPitch + grp_of(it) * 4] = ra[j];
         }
 #pragma unroll
         for (int j = 0; j < TL::LB; ++j) {
-            const int it = tid + j * kThreads;
-            *(f4*)&Bs[buf][row_of(it) * kPitch + grp_of(it) * 4] = rb[j];
+            const int it = tid + j * TL::NT;
+            if (TL::IB % TL::NT == 0 || it < TL::IB) *(f4*)&Bs[buf][row_of(it) * kPitch + grp_of(it) * 4] = rb[j];
         }
     };
 
@@ -112,18 +114,23 @@ __global__ __launch_bounds__(kThreads) void gemm_lse_partials(
     for (int kt = 0; kt < nk; ++kt) {
         const int cur = kt & 1;
         if (kt + 1 < nk) gload((kt + 1) * BK);
-        f4 a[TL::MB], b[TL::NB];
 #pragma unroll
-        for (int j = 0; j < TL::MB; ++j) a[j] = *(const f4*)&As[cur][(rm0 + j * 16 + i) * kPitch + 4 * g];
+        for (int kk = 0; kk < BK / 16; ++kk) {
+            f4 a[TL::MB], b[TL::NB];
 #pragma unroll
-        for (int j = 0; j < TL::NB; ++j) b[j] = *(const f4*)&Bs[cur][(rn0 + j * 16 + i) * kPitch + 4 * g];
+            for (int j = 0; j < TL::MB; ++j)
+                a[j] = *(const f4*)&As[cur][(rm0 + j * 16 + i) * kPitch + kk * 16 + 4 * g];
 #pragma unroll
-        for (int s = 0; s < 4; ++s)
+            for (int j = 0; j < TL::NB; ++j)
+                b[j] = *(const f4*)&Bs[cur][(rn0 + j * 16 + i) * kPitch + kk * 16 + 4 * g];
 #pragma unroll
-            for (int jm = 0; jm < TL::MB; ++jm)
+            for (int s = 0; s < 4; ++s)
 #pragma unroll
-                for (int jn = 0; jn < TL::NB; ++jn)
-                    acc[jm][jn] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[jm][s], b[jn][s], acc[jm][jn], 0, 0, 0);
+                for (int jm = 0; jm < TL::MB; ++jm)
+#pragma unroll
+                    for (int jn = 0; jn < TL::NB; ++jn)
+                        acc[jm][jn] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[jm][s], b[jn][s], acc[jm][jn], 0, 0, 0);
+        }
         if (kt + 1 < nk) sstore(cur ^ 1);
         __syncthreads();
     }
@@ -228,10 +235,10 @@ hipError_t launch_gemm_lse(const GemmPlan& p, const float* x, const float* w, co
     const unsigned grid = (unsigned)(p.tilesM * p.tilesN);
     if (timer) timer->begin("gemm_lse_partials", stream);
     if (p.vec)
-        hipLaunchKernelGGL((gemm_lse_partials<GTileA, true>), dim3(grid), dim3(kThreads), 0, stream, x, w, b,
+        hipLaunchKernelGGL((gemm_lse_partials<GTileA, true>), dim3(grid), dim3(GTileA::NT), 0, stream, x, w, b,
                            part, p.M, p.K, p.N, scale, cmin, cmax, p.tilesN);
     else
-        hipLaunchKernelGGL((gemm_lse_partials<GTileA, false>), dim3(grid), dim3(kThreads), 0, stream, x, w, b,
+        hipLaunchKernelGGL((gemm_lse_partials<GTileA, false>), dim3(grid), dim3(GTileA::NT), 0, stream, x, w, b,
                            part, p.M, p.K, p.N, scale, cmin, cmax, p.tilesN);
     hipError_t e = hipGetLastError();
     if (timer) timer->end("gemm_lse_partials", stream);
