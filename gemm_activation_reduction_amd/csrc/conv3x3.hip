@@ -185,13 +185,12 @@ struct HaloVec {
                 if constexpr (!BF16) {
                     o = u4{v[j][0][p], v[j][1][p], v[j][2][p], v[j][3][p]};
                 } else {
-                    const int dw = p >> 1, sh = (p & 1) * 16;
+                    // pixel p of channels 2k and 2k+1: one byte permute per output dword
+                    const int dw = p >> 1;
+                    const unsigned sel = (p & 1) ? 0x07060302u : 0x05040100u;
 #pragma unroll
-                    for (int k = 0; k < 4; ++k) {
-                        const unsigned lo = (v[j][2 * k][dw] >> sh) & 0xFFFFu;
-                        const unsigned hi = (v[j][2 * k + 1][dw] >> sh) & 0xFFFFu;
-                        o[k] = lo | (hi << 16);
-                    }
+                    for (int k = 0; k < 4; ++k)
+                        o[k] = __builtin_amdgcn_perm(v[j][2 * k + 1][dw], v[j][2 * k][dw], sel);
                 }
                 *(u4*)(halo + (r * TL::HP + col) * kRow + q * 16) = o;
             }
