@@ -63,6 +63,12 @@ def _load():
                                              ctypes.c_double, ci, ip, dp, dp]
         lib.oracle_lse_mish_rows.argtypes = [dp, ci, ci, dp, dp]
         lib.oracle_num_threads.restype = ci
+        lib.oracle_act_mean.argtypes = [vp, ctypes.c_longlong, ci]
+        lib.oracle_act_mean.restype = ctypes.c_double
+        lib.oracle_act_pool_map.argtypes = [vp, ci, ci, ci, ci, ci, dp]
+        lib.oracle_act_elementwise.argtypes = [vp, ctypes.c_longlong, ci, dp]
+        lib.oracle_scale_clamp_lse_mish.argtypes = [vp, ci, ci, ctypes.c_double, ctypes.c_double,
+                                                    ctypes.c_double, dp, dp]
         _lib = lib
     return _lib
 
@@ -190,4 +196,45 @@ def lse_mish_rows(c) -> tuple[np.ndarray, np.ndarray]:
     rc = _load().oracle_lse_mish_rows(_dptr(c), M, N, _dptr(out), _dptr(z))
     if rc != 0:
         raise ValueError(f"oracle_lse_mish_rows rc={rc}")
+    return out, z
+
+
+# ----------------------------------------------------------------------------- epilogue-only
+def act_mean(v, act: int) -> float:
+    """Mean of act(v) over a float32 array (one pooled value)."""
+    v = np.ascontiguousarray(v, dtype=np.float32)
+    return float(_load().oracle_act_mean(_ptr(v), v.size, int(act)))
+
+
+def act_pool_map(x, act: int) -> np.ndarray:
+    """(N, C) fp64 means of act(x) over each H x W map of a float32 NCHW array."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    N, C, H, W = x.shape
+    out = np.empty((N, C), dtype=np.float64)
+    rc = _load().oracle_act_pool_map(_ptr(x), N, C, H, W, int(act), _dptr(out))
+    if rc != 0:
+        raise ValueError(f"oracle_act_pool_map rc={rc}")
+    return out
+
+
+def act_elementwise(x, act: int) -> np.ndarray:
+    """fp64 act(x) elementwise (same shape)."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    out = np.empty(x.shape, dtype=np.float64)
+    rc = _load().oracle_act_elementwise(_ptr(x), x.size, int(act), _dptr(out))
+    if rc != 0:
+        raise ValueError(f"oracle_act_elementwise rc={rc}")
+    return out
+
+
+def scale_clamp_lse_mish(y, scale: float, cmin: float, cmax: float):
+    """(out, z) fp64 per row of a float32 [M][N] matrix: clamp(scale*y) -> logsumexp -> z*mish(z)."""
+    y = np.ascontiguousarray(y, dtype=np.float32)
+    M, N = y.shape
+    out = np.empty(M, dtype=np.float64)
+    z = np.empty(M, dtype=np.float64)
+    rc = _load().oracle_scale_clamp_lse_mish(_ptr(y), M, N, float(scale), float(cmin), float(cmax),
+                                             _dptr(out), _dptr(z))
+    if rc != 0:
+        raise ValueError(f"oracle_scale_clamp_lse_mish rc={rc}")
     return out, z

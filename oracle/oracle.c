@@ -228,3 +228,60 @@ int oracle_num_threads(void) {
     return 1;
 #endif
 }
+
+/* ---------------------------------------------------------------------------------
+ * Epilogue-only operations: the pages' own kernels that run after a separate
+ * convolution or GEMM ("Kimi-K2.6 l2_p67": GELU + average pool over the conv output;
+ * "Kimi-K2.6 l2_p4": Mish applied twice, elementwise, over the conv output;
+ * "Kimi-K2.6 l2_p22": scale, clamp, row logsumexp and x*mish(x) over the Linear output).
+ * --------------------------------------------------------------------------------- */
+
+/* mean over count values of act(v[i]) */
+double oracle_act_mean(const float* v, long long count, int act) {
+    double s = 0.0;
+    for (long long i = 0; i < count; ++i) s += oracle_act((double)v[i], act);
+    return s / (double)count;
+}
+
+/* out[n][c] = mean over the H x W map of act(x[n][c][.][.]) */
+int oracle_act_pool_map(const float* x, int N, int C, int H, int W, int act, double* out) {
+    if (!x || !out || N <= 0 || C <= 0 || H <= 0 || W <= 0) return -1;
+    long long planes = (long long)N * C, hw = (long long)H * W;
+#pragma omp parallel for schedule(dynamic)
+    for (long long p = 0; p < planes; ++p) out[p] = oracle_act_mean(x + p * hw, hw, act);
+    return 0;
+}
+
+/* out[i] = act(x[i]) */
+int oracle_act_elementwise(const float* x, long long count, int act, double* out) {
+    if (!x || !out || count < 0) return -1;
+#pragma omp parallel for schedule(static)
+    for (long long i = 0; i < count; ++i) out[i] = oracle_act((double)x[i], act);
+    return 0;
+}
+
+/* For each row of a given [M][N] matrix y: c = min(max(scale * y, cmin), cmax),
+ * z = max-shifted logsumexp of the row, out = z * mish(z). */
+int oracle_scale_clamp_lse_mish(const float* y, int M, int N, double scale, double cmin, double cmax,
+                                double* out, double* z_out) {
+    if (!y || !out || M <= 0 || N <= 0 || cmin > cmax) return -1;
+    int bad = 0;
+#pragma omp parallel for schedule(dynamic)
+    for (int m = 0; m < M; ++m) {
+        const float* r = y + (size_t)m * N;
+        double* c = (double*)malloc((size_t)N * sizeof(double));
+        if (!c) { bad = 1; continue; }
+        double mx = -INFINITY;
+        for (int j = 0; j < N; ++j) {
+            c[j] = fmin(fmax(scale * (double)r[j], cmin), cmax);
+            if (c[j] > mx) mx = c[j];
+        }
+        double s = 0.0;
+        for (int j = 0; j < N; ++j) s += exp(c[j] - mx);
+        double z = mx + log(s);
+        out[m] = z * oracle_mish(z);
+        if (z_out) z_out[m] = z;
+        free(c);
+    }
+    return bad ? -2 : 0;
+}

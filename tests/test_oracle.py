@@ -332,3 +332,67 @@ def test_gemm_bias_is_added_before_scale():
     b = np.array([0.5, 0.5, 0.5], np.float32)
     _, z = oracle.gemm_lse_mish(X, W, b, 4.0, -10.0, 10.0)
     assert z[0] == pytest.approx(2.0 + math.log(3), rel=1e-15)
+
+
+# ------------------------------------------------------------------ epilogue-only operations
+@pytest.mark.parametrize("act", [oracle.ACT_NONE, oracle.ACT_GELU, oracle.ACT_MISH2])
+def test_act_pool_map_matches_numpy(act):
+    r = np.random.default_rng(100 + act)
+    x = r.normal(scale=2.0, size=(3, 5, 7, 9)).astype(np.float32)
+    got = oracle.act_pool_map(x, act)
+    ref = np_act(x.astype(np.float64), act).mean(axis=(2, 3))
+    np.testing.assert_allclose(got, ref, rtol=1e-13, atol=1e-14)
+
+
+def test_act_pool_map_constant_map_and_divisor():
+    x = np.full((2, 3, 4, 6), -0.75, np.float32)
+    for act in (oracle.ACT_GELU, oracle.ACT_MISH2):
+        np.testing.assert_allclose(oracle.act_pool_map(x, act), np.full((2, 3), oracle.act(-0.75, act)), rtol=1e-15)
+    x = np.zeros((1, 1, 5, 8), np.float32)
+    x[0, 0, 4, 7] = 40.0  # act none: a single non-zero element divided by the whole map
+    assert oracle.act_pool_map(x, oracle.ACT_NONE)[0, 0] == pytest.approx(1.0, rel=1e-15)
+
+
+def test_act_pool_map_equals_conv_oracle_on_its_output():
+    N, Cin, H, W, Cout = 2, 3, 9, 8, 4
+    x, w, b = rng_case(123, N, Cin, H, W, Cout)
+    pre = oracle.conv_act_pool(x, w, b, oracle.ACT_NONE, 0)
+    for act in (oracle.ACT_GELU, oracle.ACT_MISH2):
+        fused = oracle.conv_act_pool(x, w, b, act, 1)
+        np.testing.assert_allclose(oracle.act_pool_map(pre.astype(np.float32), act), fused, rtol=0, atol=1e-6)
+
+
+@pytest.mark.parametrize("act", [oracle.ACT_NONE, oracle.ACT_GELU, oracle.ACT_MISH2])
+def test_act_elementwise_matches_numpy(act):
+    x = np.linspace(-30, 30, 1001).astype(np.float32)
+    # atol: for v << 0 the exact-form GELU's 1 + erf(v/sqrt2) cancels in fp64 (|error| < 1e-15)
+    np.testing.assert_allclose(oracle.act_elementwise(x, act), np_act(x.astype(np.float64), act), rtol=1e-13,
+                               atol=1e-15)
+
+
+def test_scale_clamp_lse_mish_matches_scipy_and_gemm_oracle():
+    r = np.random.default_rng(5)
+    y = r.normal(scale=3.0, size=(6, 333)).astype(np.float32)
+    for scale, cmin, cmax in [(4.0, -10.0, 10.0), (-1.5, -2.0, 0.5)]:
+        out, z = oracle.scale_clamp_lse_mish(y, scale, cmin, cmax)
+        c = np.clip(scale * y.astype(np.float64), cmin, cmax)
+        rz = scipy.special.logsumexp(c, axis=1)
+        np.testing.assert_allclose(z, rz, rtol=1e-13)
+        np.testing.assert_allclose(out, rz * np_mish(rz), rtol=1e-13)
+    # the GEMM path is this function applied to the Linear output (up to fp32 rounding of y)
+    X = r.normal(size=(4, 16)).astype(np.float32)
+    W = r.uniform(-0.3, 0.3, (50, 16)).astype(np.float32)
+    b = r.uniform(-0.3, 0.3, 50).astype(np.float32)
+    y32 = (X.astype(np.float64) @ W.T.astype(np.float64) + b).astype(np.float32)
+    o1, _ = oracle.gemm_lse_mish(X, W, b, 4.0, -10.0, 10.0)
+    o2, _ = oracle.scale_clamp_lse_mish(y32, 4.0, -10.0, 10.0)
+    np.testing.assert_allclose(o1, o2, rtol=1e-6)
+
+
+def test_scale_clamp_lse_constant_rows_and_worked_example():
+    g = json.load(open(os.path.join(GOLDEN, "lse_all_clamped.json")))
+    y = np.full((2, g["N"]), 7.0, np.float32)  # 4 * 7 = 28 -> clamped to 10 everywhere
+    out, z = oracle.scale_clamp_lse_mish(y, 4.0, -10.0, g["clamp_value"])
+    assert np.all(np.abs(z - g["lse_approx"]) < g["lse_approx_tol"])
+    assert np.all(np.abs(out - g["out_approx"]) < g["out_approx_tol"])
+    np.testing.assert_allclose(z, 10.0 + math.log(g["N"]), rtol=1e-15)

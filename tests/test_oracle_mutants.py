@@ -34,6 +34,10 @@ MUTANTS = {
     "gemm_w_transposed": ("dot += (double)xr[k] * (double)wr[k];",
                           "dot += (double)xr[k] * (double)Wt[(size_t)k * N + j];"),
     "out_missing_z_factor": ("out[i] = z * oracle_mish(z);", "out[i] = oracle_mish(z);"),
+    "act_mean_wrong_divisor": ("return s / (double)count;", "return s / (double)(count + 1);"),
+    "lse_rows_scale_dropped": ("c[j] = fmin(fmax(scale * (double)r[j], cmin), cmax);",
+                               "c[j] = fmin(fmax((double)r[j], cmin), cmax);"),
+    "lse_rows_missing_z_factor": ("out[m] = z * oracle_mish(z);", "out[m] = oracle_mish(z);"),
 }
 
 
