@@ -33,6 +33,7 @@ HBM_GBPS = 8000.0
 DEFAULT_WORKLOAD = "conv_gelu_pool_f32"
 KERNEL_SOURCES = ["gemm_activation_reduction_amd/csrc/conv3x3.hip",
                   "gemm_activation_reduction_amd/csrc/gemm_lse.hip",
+                  "gemm_activation_reduction_amd/csrc/epilogue.hip",
                   "gemm_activation_reduction_amd/csrc/device_math.h"]
 
 
@@ -144,13 +145,98 @@ def cpu_baseline_gemm(spec, X, W, b, got, seconds):
             "sample_max_err": float(max(errs)) if errs else None}
 
 
+def bench_epilogue(args, name, spec, torch, fc, dev) -> int:
+    """HBM-bound epilogue-only kernels: GB/s of algorithmic traffic against 8 TB/s."""
+    print(f"bench: generating inputs for {name}", file=sys.stderr, flush=True)
+    base = synth.epilogue_base(spec)
+    shape = spec["shape"]
+    total = int(np.prod(shape))
+    reps = total // base.size
+    bd = torch.from_numpy(base).to(dev)
+    xd = torch.cat([bd.repeat(reps), bd[: total - reps * base.size]]).view(*shape)
+    del bd
+    kind = spec["kind"]
+    if kind == "pool":
+        N, C, H, W = shape
+        out = torch.empty((N, C), dtype=torch.float32, device=dev)
+        nbytes, kernel = 4.0 * (total + N * C), "act_pool_map"
+        step = lambda: fc.fact_pool(xd, N, C, H, W, spec["act"], out)  # noqa: E731
+    elif kind == "elementwise":
+        out = torch.empty_like(xd)
+        nbytes, kernel = 8.0 * total, "act_elementwise"
+        step = lambda: fc.fact_elementwise(xd, total, spec["act"], out)  # noqa: E731
+    else:
+        M, N = shape
+        out = torch.empty((M, 1), dtype=torch.float32, device=dev)
+        nbytes, kernel = 4.0 * (total + M), "scale_clamp_lse"
+        step = lambda: fc.flse_mish_rows(xd, M, N, spec["scale"], spec["cmin"], spec["cmax"], out)  # noqa: E731
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    fc.fconv_profile(True)
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    kms, kl = fc.fconv_profile_read(kernel)
+    fc.fconv_profile(False)
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    kernel_ms = kms / max(1, kl)
+    value = nbytes / (ms_per_step * 1e-3) / 1e9
+    achieved = nbytes / (kernel_ms * 1e-3) / 1e9
+    print(f"bench: {ms_per_step:.4f} ms/step, {kernel} {kernel_ms:.4f} ms/launch, {achieved:.1f} GB/s",
+          file=sys.stderr, flush=True)
+    cpu = None
+    if args.cpu_seconds > 0:
+        import oracle
+        r = np.random.default_rng(4)
+        t0, done, work = time.perf_counter(), 0, 0
+        while time.perf_counter() - t0 < args.cpu_seconds:
+            if kind == "pool":
+                hw = shape[2] * shape[3]
+                p = int(r.integers(0, shape[0] * shape[1]))
+                oracle.act_mean(base[synth.epilogue_element_indices(spec, p * hw + np.arange(hw))], spec["act"])
+                work += 4 * hw
+            elif kind == "elementwise":
+                idx = r.integers(0, total, 1 << 20)
+                oracle.act_elementwise(base[synth.epilogue_element_indices(spec, idx)], spec["act"])
+                work += 8 * len(idx)
+            else:
+                N = shape[1]
+                m = int(r.integers(0, shape[0]))
+                y = base[synth.epilogue_element_indices(spec, m * N + np.arange(N))].reshape(1, N)
+                oracle.scale_clamp_lse_mish(y, spec["scale"], spec["cmin"], spec["cmax"])
+                work += 4 * N
+            done += 1
+        el = time.perf_counter() - t0
+        cpu = {"value": round(work / el / 1e9, 4), "unit": "GB/s", "cores": oracle.num_threads(), "kind": "oracle",
+               "seconds": round(el, 3), "sample": f"{done} sampled {'maps' if kind == 'pool' else 'batches/rows'}"}
+    line = {
+        "metric": f"epilogue-only {name} GB/s", "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": name, "shape": list(shape), "kind": kind},
+        "roofline": {"bound": "hbm", "kernel": kernel, "achieved": round(achieved, 1), "peak": HBM_GBPS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_GBPS, 4), "traffic": read_traffic(name, kernel),
+                     "kernel_ms": round(kernel_ms, 5), "algorithmic_bytes": nbytes},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD,
-                    choices=sorted(list(synth.CONV_WORKLOADS) + list(synth.GEMM_WORKLOADS)))
+                    choices=sorted(list(synth.CONV_WORKLOADS) + list(synth.GEMM_WORKLOADS)
+                                   + list(synth.EPILOGUE_WORKLOADS)))
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="oracle time budget (0: skip)")
     ap.add_argument("--calib-copy-mb", type=int, default=0,
                     help="after timing, run plain device copies of this size (HBM counter calibration)")
@@ -165,6 +251,8 @@ def main() -> int:
 
     dev = torch.device("cuda:0")
     name = args.workload
+    if name in synth.EPILOGUE_WORKLOADS:
+        return bench_epilogue(args, name, synth.EPILOGUE_WORKLOADS[name], torch, fc, dev)
     is_conv = name in synth.CONV_WORKLOADS
     spec = synth.CONV_WORKLOADS[name] if is_conv else synth.GEMM_WORKLOADS[name]
     print(f"bench: generating inputs for {name}", file=sys.stderr, flush=True)

@@ -29,8 +29,8 @@ DT_F32, DT_BF16 = 0x000, 0x100
 _ACT_NAMES = {"none": ACT_NONE, "gelu": ACT_GELU, "mish2": ACT_MISH2}
 
 # Symbols the C header declares; the loader checks that every one is exported.
-EXPORTS = ("fconv_act_pool", "fgemm_lse_mish", "fconv_last_error", "fconv_release", "fconv_version",
-           "fconv_profile", "fconv_profile_read")
+EXPORTS = ("fconv_act_pool", "fgemm_lse_mish", "fact_pool", "fact_elementwise", "flse_mish_rows",
+           "fconv_last_error", "fconv_release", "fconv_version", "fconv_profile", "fconv_profile_read")
 
 
 class FconvError(RuntimeError):
@@ -67,6 +67,12 @@ def load_library() -> ctypes.CDLL:
     lib.fconv_profile_read.argtypes = [ctypes.c_char_p, ctypes.POINTER(ctypes.c_double),
                                        ctypes.POINTER(ctypes.c_longlong)]
     lib.fconv_profile_read.restype = ci
+    lib.fact_pool.argtypes = [vp, ci, ci, ci, ci, ci, vp, vp]
+    lib.fact_pool.restype = ci
+    lib.fact_elementwise.argtypes = [vp, ctypes.c_longlong, ci, vp, vp]
+    lib.fact_elementwise.restype = ci
+    lib.flse_mish_rows.argtypes = [vp, ci, ci, cf, cf, cf, vp, vp]
+    lib.flse_mish_rows.restype = ci
     for name in EXPORTS:
         getattr(lib, name)
     _lib = lib
@@ -132,6 +138,22 @@ def fgemm_lse_mish(x, w, b, M, K, N, scale, cmin, cmax, out, stream=None) -> Non
     _check(rc)
 
 
+def fact_pool(x, N, C, H, W, act, out, stream=None) -> None:
+    """C ``fact_pool``: act then mean over each (n, c) map of a given float32 NCHW tensor."""
+    _check(load_library().fact_pool(_ptr(x), int(N), int(C), int(H), int(W), int(act), _ptr(out), _stream(stream)))
+
+
+def fact_elementwise(x, count, act, out, stream=None) -> None:
+    """C ``fact_elementwise``: out = act(x) elementwise over ``count`` float32 values."""
+    _check(load_library().fact_elementwise(_ptr(x), int(count), int(act), _ptr(out), _stream(stream)))
+
+
+def flse_mish_rows(y, M, N, scale, cmin, cmax, out, stream=None) -> None:
+    """C ``flse_mish_rows``: clamp(scale*y) -> row logsumexp -> z*mish(z) over a given [M][N] matrix."""
+    _check(load_library().flse_mish_rows(_ptr(y), int(M), int(N), float(scale), float(cmin), float(cmax),
+                                         _ptr(out), _stream(stream)))
+
+
 def _act_code(act) -> int:
     return _ACT_NAMES[act] if isinstance(act, str) else int(act)
 
@@ -171,6 +193,39 @@ def gemm_lse_mish(x: torch.Tensor, w: torch.Tensor, b: torch.Tensor, scale: floa
     if out is None:
         out = torch.empty((M, 1), dtype=torch.float32, device=x.device)
     fgemm_lse_mish(x, w, b, M, K, N, scale, cmin, cmax, out, stream)
+    return out
+
+
+def act_pool(x: torch.Tensor, act="gelu", out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """Tensor helper: float32 NCHW x -> (N, C) means of act(x)."""
+    if x.dtype != torch.float32 or not x.is_cuda or not x.is_contiguous():
+        raise ValueError("x must be a contiguous float32 device tensor")
+    N, C, H, W = x.shape
+    if out is None:
+        out = torch.empty((N, C), dtype=torch.float32, device=x.device)
+    fact_pool(x, N, C, H, W, _act_code(act), out, stream)
+    return out
+
+
+def act_elementwise(x: torch.Tensor, act="mish2", out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """Tensor helper: float32 x -> act(x) (out may be x itself)."""
+    if x.dtype != torch.float32 or not x.is_cuda or not x.is_contiguous():
+        raise ValueError("x must be a contiguous float32 device tensor")
+    if out is None:
+        out = torch.empty_like(x)
+    fact_elementwise(x, x.numel(), _act_code(act), out, stream)
+    return out
+
+
+def lse_mish_rows(y: torch.Tensor, scale: float = 4.0, cmin: float = -10.0, cmax: float = 10.0,
+                  out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """Tensor helper: float32 y (M, N) -> (M, 1)."""
+    if y.dtype != torch.float32 or not y.is_cuda or not y.is_contiguous() or y.dim() != 2:
+        raise ValueError("y must be a contiguous 2-D float32 device tensor")
+    M, N = y.shape
+    if out is None:
+        out = torch.empty((M, 1), dtype=torch.float32, device=y.device)
+    flse_mish_rows(y, M, N, scale, cmin, cmax, out, stream)
     return out
 
 

@@ -144,6 +144,19 @@ EventTimer g_timer;
 
 fconv::KernelTimer* active_timer() { return g_timer.enabled ? &g_timer : nullptr; }
 
+// Brackets a single-kernel entry point with the timer (when profiling is on).
+struct ActivePlanTimer {
+    fconv::KernelTimer* t;
+    const char* name;
+    hipStream_t s;
+    ActivePlanTimer(fconv::KernelTimer* t_, const char* n, hipStream_t s_) : t(t_), name(n), s(s_) {
+        if (t) t->begin(name, s);
+    }
+    ~ActivePlanTimer() {
+        if (t) t->end(name, s);
+    }
+};
+
 bool overlaps(const void* a, size_t abytes, const void* b, size_t bbytes) {
     const uintptr_t a0 = (uintptr_t)a, b0 = (uintptr_t)b;
     return a0 < b0 + bbytes && b0 < a0 + abytes;
@@ -209,6 +222,50 @@ FCONV_API int fgemm_lse_mish(const float* x, const float* w, const float* b, int
     if (rc != FCONV_OK) return rc;
     hipError_t e = fconv::launch_gemm_lse(plan, x, w, b, scale, cmin, cmax, out, ws, stream, active_timer());
     if (e != hipSuccess) return fail(FCONV_EHIP, std::string("fgemm_lse_mish launch: ") + hipGetErrorString(e));
+    return ok();
+}
+
+FCONV_API int fact_pool(const float* x, int N, int C, int H, int W, int act, float* out, hipStream_t stream) {
+    if (!x || !out) return fail(FCONV_EINVAL, "fact_pool: null pointer argument");
+    if (N < 1 || C < 1 || H < 1 || W < 1) return fail(FCONV_EINVAL, "fact_pool: N, C, H and W must be >= 1");
+    if (act != FCONV_ACT_NONE && act != FCONV_ACT_GELU && act != FCONV_ACT_MISH2)
+        return fail(FCONV_EINVAL, "fact_pool: act must be FCONV_ACT_NONE, _GELU or _MISH2 (float32 only)");
+    const long long nx = (long long)N * C * H * W, nout = (long long)N * C;
+    if (nx > kMaxElems) return fail(FCONV_EINVAL, "fact_pool: a tensor has 2^31 or more elements");
+    if (overlaps(out, (size_t)nout * 4, x, (size_t)nx * 4)) return fail(FCONV_EINVAL, "fact_pool: out overlaps x");
+    ActivePlanTimer t(active_timer(), "act_pool_map", stream);
+    hipError_t e = fconv::launch_act_pool_map(x, N, C, H, W, act, out, stream);
+    if (e != hipSuccess) return fail(FCONV_EHIP, std::string("fact_pool launch: ") + hipGetErrorString(e));
+    return ok();
+}
+
+FCONV_API int fact_elementwise(const float* x, long long count, int act, float* out, hipStream_t stream) {
+    if (!x || !out) return fail(FCONV_EINVAL, "fact_elementwise: null pointer argument");
+    if (count < 0) return fail(FCONV_EINVAL, "fact_elementwise: count must be >= 0");
+    if (act != FCONV_ACT_NONE && act != FCONV_ACT_GELU && act != FCONV_ACT_MISH2)
+        return fail(FCONV_EINVAL, "fact_elementwise: act must be FCONV_ACT_NONE, _GELU or _MISH2 (float32 only)");
+    if (count > (1LL << 40)) return fail(FCONV_EINVAL, "fact_elementwise: count too large");
+    if (out != x && overlaps(out, (size_t)count * 4, x, (size_t)count * 4))
+        return fail(FCONV_EINVAL, "fact_elementwise: out partially overlaps x (only out == x is allowed)");
+    ActivePlanTimer t(active_timer(), "act_elementwise", stream);
+    hipError_t e = fconv::launch_act_elementwise(x, count, act, out, stream);
+    if (e != hipSuccess) return fail(FCONV_EHIP, std::string("fact_elementwise launch: ") + hipGetErrorString(e));
+    return ok();
+}
+
+FCONV_API int flse_mish_rows(const float* y, int M, int N, float scale, float cmin, float cmax, float* out,
+                             hipStream_t stream) {
+    if (!y || !out) return fail(FCONV_EINVAL, "flse_mish_rows: null pointer argument");
+    if (M < 1 || N < 1) return fail(FCONV_EINVAL, "flse_mish_rows: M and N must be >= 1");
+    if (!std::isfinite(scale)) return fail(FCONV_EINVAL, "flse_mish_rows: scale must be finite");
+    if (std::isnan(cmin) || std::isnan(cmax) || cmin > cmax)
+        return fail(FCONV_EINVAL, "flse_mish_rows: need cmin <= cmax (not NaN)");
+    const long long ny = (long long)M * N;
+    if (ny > kMaxElems) return fail(FCONV_EINVAL, "flse_mish_rows: y has 2^31 or more elements");
+    if (overlaps(out, (size_t)M * 4, y, (size_t)ny * 4)) return fail(FCONV_EINVAL, "flse_mish_rows: out overlaps y");
+    ActivePlanTimer t(active_timer(), "scale_clamp_lse", stream);
+    hipError_t e = fconv::launch_scale_clamp_lse(y, M, N, scale, cmin, cmax, out, stream);
+    if (e != hipSuccess) return fail(FCONV_EHIP, std::string("flse_mish_rows launch: ") + hipGetErrorString(e));
     return ok();
 }
 

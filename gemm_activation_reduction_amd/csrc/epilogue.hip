@@ -1,0 +1,182 @@
+// Epilogue-only kernels: the pages' own kernels that run after a separate convolution
+// or GEMM, re-done for gfx950. All three are HBM-bound streams:
+//   act_pool_map      act + mean over each (n, c) map of a given NCHW tensor
+//                     ("Kimi-K2.6 l2_p67": GELU + AdaptiveAvgPool2d(1) over the conv output);
+//   act_elementwise   act over a given tensor ("Kimi-K2.6 l2_p4": Mish applied twice);
+//   scale_clamp_lse   scale, clamp, row logsumexp and z * mish(z) over a given [M][N]
+//                     matrix ("Kimi-K2.6 l2_p22": the fused kernel after nn.Linear).
+// Reductions are fixed-order (per-thread strided sums, wave64 butterflies, then waves
+// in order through LDS), so results are deterministic run to run.
+#include <cstdint>
+
+#include "device_math.h"
+#include "internal.h"
+
+namespace fconv {
+namespace {
+
+typedef float f4 __attribute__((ext_vector_type(4)));
+
+constexpr int kThreads = 256;
+
+// Sums one value per thread over a 256-thread workgroup in a fixed order; the result is
+// valid in thread 0.
+__device__ __forceinline__ float block_sum(float v, float* red) {
+    v = wave_sum(v);
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    if (lane == 0) red[wave] = v;
+    __syncthreads();
+    float s = 0.0f;
+    if (threadIdx.x == 0) s = ((red[0] + red[1]) + red[2]) + red[3];
+    __syncthreads();
+    return s;
+}
+
+// One workgroup per (n, c) map: sum of act(x) over the map, divided by its size.
+// VEC: the map is a whole number of 16-byte groups and 16-byte aligned.
+template <int ACT, bool VEC>
+__global__ __launch_bounds__(kThreads) void act_pool_map(const float* __restrict__ x, float* __restrict__ out,
+                                                        long long hw, float inv_count) {
+    __shared__ float red[4];
+    const float* p = x + (long long)blockIdx.x * hw;
+    float s = 0.0f;
+    if constexpr (VEC) {
+        const f4* p4 = (const f4*)p;
+        const long long n4 = hw >> 2;
+#pragma unroll 4
+        for (long long k = threadIdx.x; k < n4; k += kThreads) {
+            const f4 v = __builtin_nontemporal_load(p4 + k);
+            s += (activate<ACT>(v.x) + activate<ACT>(v.y)) + (activate<ACT>(v.z) + activate<ACT>(v.w));
+        }
+    } else {
+#pragma unroll 4
+        for (long long k = threadIdx.x; k < hw; k += kThreads) s += activate<ACT>(p[k]);
+    }
+    s = block_sum(s, red);
+    if (threadIdx.x == 0) out[blockIdx.x] = s * inv_count;
+}
+
+// out[i] = act(x[i]); out may be x. Grid-stride over 16-byte groups, then the tail.
+template <int ACT, bool VEC>
+__global__ __launch_bounds__(kThreads) void act_elementwise(const float* x, float* out, long long count) {
+    const long long stride = (long long)gridDim.x * kThreads;
+    long long k = (long long)blockIdx.x * kThreads + threadIdx.x;
+    if constexpr (VEC) {
+        const long long n4 = count >> 2;
+        for (long long q = k; q < n4; q += stride) {
+            const f4 v = __builtin_nontemporal_load((const f4*)x + q);
+            const f4 r = {activate<ACT>(v.x), activate<ACT>(v.y), activate<ACT>(v.z), activate<ACT>(v.w)};
+            __builtin_nontemporal_store(r, (f4*)out + q);
+        }
+        for (long long i = (n4 << 2) + k; i < count; i += stride) out[i] = activate<ACT>(x[i]);
+    } else {
+        for (long long i = k; i < count; i += stride) out[i] = activate<ACT>(x[i]);
+    }
+}
+
+// One workgroup per row: c = clamp(scale * y); z = M + log(sum exp(c - M)), M = max c
+// (two passes; the second reads the row back from L2), then out = z * mish(z) with the
+// overflow-free softplus max(z,0) + log1p(e^-|z|).
+template <bool VEC>
+__global__ __launch_bounds__(kThreads) void scale_clamp_lse(const float* __restrict__ y, float* __restrict__ out,
+                                                           int N, float scale, float cmin, float cmax) {
+    __shared__ float red[4];
+    __shared__ float s_max;
+    const float* r = y + (long long)blockIdx.x * N;
+    auto clampv = [&](float v) { return fminf(fmaxf(scale * v, cmin), cmax); };
+    float m = -INFINITY;
+    if constexpr (VEC) {
+        for (int k = threadIdx.x; k < (N >> 2); k += kThreads) {
+            const f4 v = ((const f4*)r)[k];
+            m = fmaxf(m, fmaxf(fmaxf(clampv(v.x), clampv(v.y)), fmaxf(clampv(v.z), clampv(v.w))));
+        }
+    } else {
+        for (int k = threadIdx.x; k < N; k += kThreads) m = fmaxf(m, clampv(r[k]));
+    }
+    m = wave_max(m);
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    if (lane == 0) red[wave] = m;
+    __syncthreads();
+    if (threadIdx.x == 0) s_max = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    __syncthreads();
+    const float mx = s_max;
+    float s = 0.0f;
+    if constexpr (VEC) {
+        for (int k = threadIdx.x; k < (N >> 2); k += kThreads) {
+            const f4 v = ((const f4*)r)[k];
+            s += (fast_exp(clampv(v.x) - mx) + fast_exp(clampv(v.y) - mx)) +
+                 (fast_exp(clampv(v.z) - mx) + fast_exp(clampv(v.w) - mx));
+        }
+    } else {
+        for (int k = threadIdx.x; k < N; k += kThreads) s += fast_exp(clampv(r[k]) - mx);
+    }
+    s = block_sum(s, red);
+    if (threadIdx.x == 0) {
+        const float z = mx + logf(s);
+        const float sp = fmaxf(z, 0.0f) + log1pf(expf(-fabsf(z)));
+        out[blockIdx.x] = z * (z * tanhf(sp));
+    }
+}
+
+template <int ACT>
+void launch_pool_typed(bool vec, const float* x, float* out, long long hw, float inv, unsigned planes,
+                       hipStream_t stream) {
+    if (vec)
+        hipLaunchKernelGGL((act_pool_map<ACT, true>), dim3(planes), dim3(kThreads), 0, stream, x, out, hw, inv);
+    else
+        hipLaunchKernelGGL((act_pool_map<ACT, false>), dim3(planes), dim3(kThreads), 0, stream, x, out, hw, inv);
+}
+
+template <int ACT>
+void launch_ew_typed(bool vec, const float* x, float* out, long long count, unsigned blocks, hipStream_t stream) {
+    if (vec)
+        hipLaunchKernelGGL((act_elementwise<ACT, true>), dim3(blocks), dim3(kThreads), 0, stream, x, out, count);
+    else
+        hipLaunchKernelGGL((act_elementwise<ACT, false>), dim3(blocks), dim3(kThreads), 0, stream, x, out, count);
+}
+
+}  // namespace
+
+hipError_t launch_act_pool_map(const float* x, int N, int C, int H, int W, int act, float* out,
+                               hipStream_t stream) {
+    const long long hw = (long long)H * W;
+    const bool vec = hw % 4 == 0 && (uintptr_t)x % 16 == 0;
+    const float inv = (float)(1.0 / (double)hw);
+    const unsigned planes = (unsigned)((long long)N * C);
+    switch (act) {
+        case kActNone: launch_pool_typed<kActNone>(vec, x, out, hw, inv, planes, stream); break;
+        case kActGelu: launch_pool_typed<kActGelu>(vec, x, out, hw, inv, planes, stream); break;
+        case kActMish2: launch_pool_typed<kActMish2>(vec, x, out, hw, inv, planes, stream); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_act_elementwise(const float* x, long long count, int act, float* out, hipStream_t stream) {
+    if (count == 0) return hipSuccess;
+    const bool vec = (uintptr_t)x % 16 == 0 && (uintptr_t)out % 16 == 0;
+    const long long groups = vec ? (count + 3) / 4 : count;
+    const long long want = (groups + kThreads - 1) / kThreads;
+    const unsigned blocks = (unsigned)(want < 8192 ? want : 8192);
+    switch (act) {
+        case kActNone: launch_ew_typed<kActNone>(vec, x, out, count, blocks, stream); break;
+        case kActGelu: launch_ew_typed<kActGelu>(vec, x, out, count, blocks, stream); break;
+        case kActMish2: launch_ew_typed<kActMish2>(vec, x, out, count, blocks, stream); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_scale_clamp_lse(const float* y, int M, int N, float scale, float cmin, float cmax, float* out,
+                                  hipStream_t stream) {
+    const bool vec = N % 4 == 0 && (uintptr_t)y % 16 == 0;
+    if (vec)
+        hipLaunchKernelGGL((scale_clamp_lse<true>), dim3((unsigned)M), dim3(kThreads), 0, stream, y, out, N, scale,
+                           cmin, cmax);
+    else
+        hipLaunchKernelGGL((scale_clamp_lse<false>), dim3((unsigned)M), dim3(kThreads), 0, stream, y, out, N, scale,
+                           cmin, cmax);
+    return hipGetLastError();
+}
+
+}  // namespace fconv

@@ -46,4 +46,11 @@ hipError_t launch_gemm_lse(const GemmPlan& p, const float* x, const float* w, co
                            float scale, float cmin, float cmax, float* out, void* workspace,
                            hipStream_t stream, KernelTimer* timer);
 
+// Epilogue-only kernels (HBM-bound streams over an already materialized tensor).
+hipError_t launch_act_pool_map(const float* x, int N, int C, int H, int W, int act, float* out,
+                               hipStream_t stream);
+hipError_t launch_act_elementwise(const float* x, long long count, int act, float* out, hipStream_t stream);
+hipError_t launch_scale_clamp_lse(const float* y, int M, int N, float scale, float cmin, float cmax, float* out,
+                                  hipStream_t stream);
+
 }  // namespace fconv

@@ -99,6 +99,30 @@ int fgemm_lse_mish(const float* x, const float* w, const float* b,
                    int M, int K, int N, float scale, float cmin, float cmax,
                    float* out, hipStream_t stream);
 
+/*
+ * Epilogue-only operations over an already materialized tensor: the kernels the pages
+ * write for use after a separate convolution or GEMM. All float32, all HBM-bound.
+ *
+ * fact_pool: out[n,c] = (1 / (H W)) * sum_{h,w} act(x[n,c,h,w]), x NCHW [N][C][H][W],
+ *   out [N][C]; act = FCONV_ACT_NONE, FCONV_ACT_GELU or FCONV_ACT_MISH2 (no dtype bits).
+ *   Source: the GELU + AdaptiveAvgPool2d(1) kernel of the "Kimi-K2.6 l2_p67" page.
+ * fact_elementwise: out[i] = act(x[i]) for 0 <= i < count; out == x (in place) is
+ *   allowed, any other overlap is not. Source: the Mish -> Mish kernel of the
+ *   "Kimi-K2.6 l2_p4" page (act = FCONV_ACT_MISH2).
+ * flse_mish_rows: for each row m of y [M][N] (row-major), c = min(max(scale y, cmin), cmax),
+ *   z = log(sum_j exp(c[m,j])) (max-shifted), out[m] = z * mish(z). Source: the fused
+ *   scale/clamp/logsumexp/mish kernel of the "Kimi-K2.6 l2_p22" page, applied to the
+ *   nn.Linear output (which already includes the bias).
+ * Errors: FCONV_EINVAL for a null pointer, a size < 1 (count < 0), an unknown act, a NaN
+ * or infinite scale, cmin > cmax or NaN, a tensor of 2^31 or more elements (fact_pool,
+ * flse_mish_rows), or a forbidden overlap; FCONV_EHIP if the launch fails. Results are
+ * deterministic run to run (fixed-order reductions). No workspace is used.
+ */
+int fact_pool(const float* x, int N, int C, int H, int W, int act, float* out, hipStream_t stream);
+int fact_elementwise(const float* x, long long count, int act, float* out, hipStream_t stream);
+int flse_mish_rows(const float* y, int M, int N, float scale, float cmin, float cmax, float* out,
+                   hipStream_t stream);
+
 /* Message describing the calling thread's last non-OK return ("" if none). The
  * pointer stays valid until the next call into the library from that thread. */
 const char* fconv_last_error(void);
@@ -115,7 +139,8 @@ int fconv_release(void);
  * fconv_profile_read(kernel, &ms, &launches) waits for the recorded events and returns
  * the summed event time in milliseconds and the number of launches of `kernel` since
  * the last fconv_profile() call. Kernel names: "pack_weights", "conv3x3_fused",
- * "pool_finalize", "gemm_lse_partials", "lse_merge_mish". Unknown names read as zero.
+ * "pool_finalize", "gemm_lse_partials", "lse_merge_mish", "act_pool_map", "act_elementwise",
+ * "scale_clamp_lse". Unknown names read as zero.
  * Returns FCONV_EINVAL for a null argument, FCONV_EHIP if an event wait fails.
  */
 int fconv_profile(int enable);

@@ -144,3 +144,29 @@ def gemm_inputs(spec: dict, seed_cfg: int | None = None):
     W = uniform(seed_for(cfg, W_ID), N * K, -spec["w_bound"], spec["w_bound"]).reshape(N, K)
     b = uniform(seed_for(cfg, B_ID), N, -spec["b_bound"], spec["b_bound"])
     return X, W, b
+
+
+# Epilogue-only workloads: the tensors the pages' own post-conv / post-GEMM kernels read.
+# A full-size tensor is a seeded N(0, 1) base of `base` elements repeated to the full
+# element count (generating 0.5 G normals on the host would take minutes); every element
+# i of the full tensor equals base[i % base].
+EPILOGUE_WORKLOADS = {
+    # the (128, 64, 254, 254) conv output of the Conv2d(8->64) -> GELU -> avg-pool page
+    "epi_gelu_pool_f32": dict(cfg=6, kind="pool", shape=(128, 64, 254, 254), act=ACT_GELU, base=1 << 24),
+    # the (64, 128, 254, 254) conv output of the Conv2d(64->128) -> Mish -> Mish page
+    "epi_mish2_f32": dict(cfg=7, kind="elementwise", shape=(64, 128, 254, 254), act=ACT_MISH2, base=1 << 24),
+    # the (1024, 8192) Linear output of the Linear -> scale -> clamp -> logsumexp -> mish page
+    "epi_lse_mish_f32": dict(cfg=8, kind="lse", shape=(1024, 8192), scale=4.0, cmin=-10.0, cmax=10.0,
+                             base=1 << 23),
+}
+
+
+def epilogue_base(spec: dict) -> np.ndarray:
+    """The seeded float32 N(0, 1) base vector of an epilogue-only workload."""
+    total = int(np.prod(spec["shape"]))
+    return normal(seed_for(spec["cfg"], X_ID), min(spec["base"], total))
+
+
+def epilogue_element_indices(spec: dict, flat_index: np.ndarray) -> np.ndarray:
+    """Positions in the base vector of the given flat indices of the full tensor."""
+    return np.asarray(flat_index, dtype=np.int64) % min(spec["base"], int(np.prod(spec["shape"])))

@@ -106,3 +106,26 @@ def test_gemm_validation(kw, frag):
 def test_last_error_is_per_call():
     conv_err(N=0)
     assert ">= 1" in fc.fconv_last_error()
+
+
+@pytest.mark.parametrize("call,frag", [
+    (lambda: fc.fact_pool(0, 1, 1, 1, 1, 1, FAKE, S0), "null"),
+    (lambda: fc.fact_pool(FAKE, 0, 1, 1, 1, 1, FAKE + (1 << 30), S0), ">= 1"),
+    (lambda: fc.fact_pool(FAKE, 1, 1, 4, 4, 0x101, FAKE + (1 << 30), S0), "act"),
+    (lambda: fc.fact_pool(FAKE, 1, 1, 4, 4, 3, FAKE + (1 << 30), S0), "act"),
+    (lambda: fc.fact_pool(FAKE, 1 << 12, 1 << 10, 1 << 5, 1 << 5, 1, FAKE + (1 << 38), S0), "2^31"),
+    (lambda: fc.fact_pool(FAKE, 2, 2, 4, 4, 1, FAKE + 16, S0), "overlaps"),
+    (lambda: fc.fact_elementwise(FAKE, -1, 1, FAKE + (1 << 30), S0), "count"),
+    (lambda: fc.fact_elementwise(FAKE, 100, 7, FAKE + (1 << 30), S0), "act"),
+    (lambda: fc.fact_elementwise(FAKE, 100, 1, FAKE + 4, S0), "overlap"),
+    (lambda: fc.fact_elementwise(0, 100, 1, FAKE, S0), "null"),
+    (lambda: fc.flse_mish_rows(FAKE, 0, 4, 4.0, -1.0, 1.0, FAKE + (1 << 30), S0), ">= 1"),
+    (lambda: fc.flse_mish_rows(FAKE, 4, 4, float("inf"), -1.0, 1.0, FAKE + (1 << 30), S0), "scale"),
+    (lambda: fc.flse_mish_rows(FAKE, 4, 4, 4.0, 2.0, 1.0, FAKE + (1 << 30), S0), "cmin"),
+    (lambda: fc.flse_mish_rows(FAKE, 4, 4, 4.0, -1.0, 1.0, FAKE + 8, S0), "overlaps"),
+])
+def test_epilogue_validation(call, frag):
+    with pytest.raises(fc.FconvError) as e:
+        call()
+    assert e.value.code == fc.FCONV_EINVAL
+    assert frag in e.value.message
