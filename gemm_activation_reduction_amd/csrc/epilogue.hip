@@ -63,11 +63,17 @@ __global__ __launch_bounds__(kThreads) void act_elementwise(const float* x, floa
     long long k = (long long)blockIdx.x * kThreads + threadIdx.x;
     if constexpr (VEC) {
         const long long n4 = count >> 2;
-        for (long long q = k; q < n4; q += stride) {
-            const f4 v = __builtin_nontemporal_load((const f4*)x + q);
-            const f4 r = {activate<ACT>(v.x), activate<ACT>(v.y), activate<ACT>(v.z), activate<ACT>(v.w)};
-            __builtin_nontemporal_store(r, (f4*)out + q);
+        auto act4 = [](f4 v) { return f4{activate<ACT>(v.x), activate<ACT>(v.y), activate<ACT>(v.z), activate<ACT>(v.w)}; };
+        long long q = k;
+        // four 16-byte groups in flight per thread
+        for (; q + 3 * stride < n4; q += 4 * stride) {
+            f4 v[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) v[u] = __builtin_nontemporal_load((const f4*)x + q + u * stride);
+#pragma unroll
+            for (int u = 0; u < 4; ++u) __builtin_nontemporal_store(act4(v[u]), (f4*)out + q + u * stride);
         }
+        for (; q < n4; q += stride) __builtin_nontemporal_store(act4(__builtin_nontemporal_load((const f4*)x + q)), (f4*)out + q);
         for (long long i = (n4 << 2) + k; i < count; i += stride) out[i] = activate<ACT>(x[i]);
     } else {
         for (long long i = k; i < count; i += stride) out[i] = activate<ACT>(x[i]);
