@@ -23,7 +23,7 @@ _LIB = os.path.join(_HERE, "liboracle.so")
 # A test that plants mistakes in a copy of the oracle points this at the copy.
 _LIB = os.environ.get("ORACLE_LIB_OVERRIDE", _LIB)
 
-ACT_NONE, ACT_GELU, ACT_MISH2 = 0, 1, 2
+ACT_NONE, ACT_GELU, ACT_MISH2, ACT_GELU_TANH = 0, 1, 2, 3
 
 
 def build(force: bool = True) -> str:
@@ -52,7 +52,7 @@ def _load():
         ci = ctypes.c_int
         lib.oracle_act.argtypes = [ctypes.c_double, ci]
         lib.oracle_act.restype = ctypes.c_double
-        for f in ("oracle_gelu", "oracle_mish", "oracle_softplus"):
+        for f in ("oracle_gelu", "oracle_gelu_tanh", "oracle_mish", "oracle_softplus"):
             getattr(lib, f).argtypes = [ctypes.c_double]
             getattr(lib, f).restype = ctypes.c_double
         lib.oracle_conv_act_pool.argtypes = [vp, vp, vp, ci, ci, ci, ci, ci, ci, ci, ci, dp]
@@ -99,6 +99,10 @@ def act(v: float, kind: int) -> float:
 
 def gelu(v: float) -> float:
     return _load().oracle_gelu(float(v))
+
+
+def gelu_tanh(v: float) -> float:
+    return _load().oracle_gelu_tanh(float(v))
 
 
 def mish(v: float) -> float:

@@ -13,7 +13,9 @@
  *    size H-2; Mish = x * tanh(softplus(x)) applied twice.
  *  - "Kimi-K2.6 l2_p67" (Conv2d -> GELU -> AdaptiveAvgPool2d(1)): the exact
  *    erf form of GELU (PyTorch's approximate='none'), then the mean of each
- *    (n, c) feature map over the valid output positions.
+ *    (n, c) feature map over the valid output positions. The same page also
+ *    writes the tanh approximation of GELU (PyTorch's approximate='tanh'),
+ *    offered here as a separate activation.
  *  - "Kimi-K2.6 l2_p22" (Linear -> scale -> x+x -> clamp -> logsumexp ->
  *    x*mish(x)): y = x W^T + b, scaled (the page's x2 then x+x is x4),
  *    clamped, the max-shifted logsumexp per row, then z * mish(z).
@@ -36,6 +38,7 @@
 #define ORACLE_ACT_NONE 0
 #define ORACLE_ACT_GELU 1
 #define ORACLE_ACT_MISH2 2
+#define ORACLE_ACT_GELU_TANH 3
 
 static double widen_bf16(uint16_t bits) {
     uint32_t u = ((uint32_t)bits) << 16;
@@ -65,11 +68,19 @@ double oracle_gelu(double v) {
     return 0.5 * v * (1.0 + erf(v / sqrt(2.0)));
 }
 
-/* Pointwise activation: 0 none, 1 exact GELU, 2 Mish applied twice. */
+/* Tanh approximation of GELU (l2_p67 page, where it weighs the tanh form against
+ * the exact one): 0.5 v (1 + tanh(sqrt(2/pi) (v + 0.044715 v^3))). */
+double oracle_gelu_tanh(double v) {
+    const double k = sqrt(2.0 / 3.14159265358979323846); /* sqrt(2 / pi) */
+    return 0.5 * v * (1.0 + tanh(k * (v + 0.044715 * v * v * v)));
+}
+
+/* Pointwise activation: 0 none, 1 exact GELU, 2 Mish applied twice, 3 tanh GELU. */
 double oracle_act(double v, int act) {
     switch (act) {
         case ORACLE_ACT_GELU: return oracle_gelu(v);
         case ORACLE_ACT_MISH2: return oracle_mish(oracle_mish(v));
+        case ORACLE_ACT_GELU_TANH: return oracle_gelu_tanh(v);
         default: return v;
     }
 }

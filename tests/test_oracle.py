@@ -30,6 +30,11 @@ def np_gelu(v):
     return v * scipy.special.ndtr(v)
 
 
+def np_gelu_tanh(v):
+    # 0.5 (1 + tanh(u)) = sigmoid(2u): the page's tanh form evaluated through the logistic function
+    return v * scipy.special.expit(2.0 * math.sqrt(2.0 / math.pi) * (v + 0.044715 * v ** 3))
+
+
 def np_mish(v):
     return v * np.tanh(np.logaddexp(0.0, v))
 
@@ -39,6 +44,8 @@ def np_act(v, act):
         return np_gelu(v)
     if act == oracle.ACT_MISH2:
         return np_mish(np_mish(v))
+    if act == oracle.ACT_GELU_TANH:
+        return np_gelu_tanh(v)
     return v
 
 
@@ -76,6 +83,29 @@ def test_gelu_matches_normal_cdf_and_reflection():
         assert oracle.gelu(-v) == pytest.approx(g - v, abs=1e-13)
 
 
+def test_gelu_tanh_logistic_form_and_reflection():
+    for v in np.linspace(-10, 10, 201):
+        g = oracle.gelu_tanh(v)
+        assert oracle.act(v, oracle.ACT_GELU_TANH) == g
+        assert g == pytest.approx(np_gelu_tanh(v), rel=1e-13, abs=1e-15)
+        # tanh is odd  =>  GELU_tanh(v) - GELU_tanh(-v) = v
+        assert g - oracle.gelu_tanh(-v) == pytest.approx(v, abs=1e-13)
+    assert oracle.gelu_tanh(0.0) == 0.0
+    assert oracle.gelu_tanh(30.0) == 30.0
+    assert abs(oracle.gelu_tanh(-30.0)) < 1e-300
+
+
+def test_gelu_tanh_is_the_close_approximation_of_exact_gelu():
+    # The tanh form approximates v * Phi(v) to within 4.8e-4 everywhere (the cubic
+    # coefficient is fitted for that); its largest gap, 4.73e-4, sits near |v| = 2.70.
+    # A dropped cubic term or a wrong constant moves the gap to 1e-3 .. 3e-2.
+    vs = np.linspace(-12, 12, 24001)
+    d = np.array([oracle.gelu_tanh(v) for v in vs]) - np_gelu(vs)
+    assert np.max(np.abs(d)) < 4.8e-4
+    assert np.max(np.abs(d)) > 4.6e-4
+    assert abs(abs(vs[np.argmax(np.abs(d))]) - 2.70) < 0.05  # the gap is even in v
+
+
 def test_softplus_matches_logaddexp():
     for v in np.concatenate([np.linspace(-50, 50, 201), [-700.0, 700.0]]):
         assert oracle.softplus(v) == pytest.approx(np.logaddexp(0.0, v), rel=1e-14, abs=1e-300)
@@ -111,7 +141,7 @@ def test_mish2_is_composition():
 
 
 # ------------------------------------------------------------------ convolution
-@pytest.mark.parametrize("act", [oracle.ACT_NONE, oracle.ACT_GELU, oracle.ACT_MISH2])
+@pytest.mark.parametrize("act", [oracle.ACT_NONE, oracle.ACT_GELU, oracle.ACT_MISH2, oracle.ACT_GELU_TANH])
 @pytest.mark.parametrize("shape", [(2, 3, 16, 16, 8), (3, 5, 9, 11, 7), (1, 1, 3, 3, 1), (2, 4, 3, 7, 3)])
 def test_conv_matches_bruteforce(act, shape):
     N, Cin, H, W, Cout = shape
@@ -335,7 +365,7 @@ def test_gemm_bias_is_added_before_scale():
 
 
 # ------------------------------------------------------------------ epilogue-only operations
-@pytest.mark.parametrize("act", [oracle.ACT_NONE, oracle.ACT_GELU, oracle.ACT_MISH2])
+@pytest.mark.parametrize("act", [oracle.ACT_NONE, oracle.ACT_GELU, oracle.ACT_MISH2, oracle.ACT_GELU_TANH])
 def test_act_pool_map_matches_numpy(act):
     r = np.random.default_rng(100 + act)
     x = r.normal(scale=2.0, size=(3, 5, 7, 9)).astype(np.float32)
@@ -362,7 +392,7 @@ def test_act_pool_map_equals_conv_oracle_on_its_output():
         np.testing.assert_allclose(oracle.act_pool_map(pre.astype(np.float32), act), fused, rtol=0, atol=1e-6)
 
 
-@pytest.mark.parametrize("act", [oracle.ACT_NONE, oracle.ACT_GELU, oracle.ACT_MISH2])
+@pytest.mark.parametrize("act", [oracle.ACT_NONE, oracle.ACT_GELU, oracle.ACT_MISH2, oracle.ACT_GELU_TANH])
 def test_act_elementwise_matches_numpy(act):
     x = np.linspace(-30, 30, 1001).astype(np.float32)
     # atol: for v << 0 the exact-form GELU's 1 + erf(v/sqrt2) cancels in fp64 (|error| < 1e-15)

@@ -26,6 +26,9 @@ MUTANTS = {
     "dropped_bias": ("return acc + (double)b[oc];", "return acc;"),
     "gelu_wrong_constant": ("erf(v / sqrt(2.0))", "erf(v / 2.0)"),
     "gelu_wrong_sign": ("(1.0 + erf(", "(1.0 - erf("),
+    "gelu_tanh_no_cubic": ("(v + 0.044715 * v * v * v)", "(v)"),
+    "gelu_tanh_wrong_constant": ("0.044715", "0.04715"),
+    "gelu_tanh_half_dropped": ("return 0.5 * v * (1.0 + tanh(", "return v * (1.0 + tanh("),
     "softplus_wrong_sign": ("log1p(exp(-fabs(v)))", "log1p(exp(fabs(v)))"),
     "single_mish": ("return oracle_mish(oracle_mish(v));", "return oracle_mish(v);"),
     "pool_divisor_full_map": ("((double)OH * (double)OW)", "((double)H * (double)W)"),
