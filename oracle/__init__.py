@@ -59,7 +59,7 @@ def _load():
         lib.oracle_conv_pool_sample.argtypes = [vp, vp, vp, ci, ci, ci, ci, ci, ci, ci, ci, ip, ip, dp]
         lib.oracle_conv_point_sample.argtypes = [vp, vp, vp, ci, ci, ci, ci, ci, ci, ci, ci,
                                                  ip, ip, ip, ip, dp]
-        lib.oracle_gemm_lse_mish.argtypes = [vp, vp, vp, ci, ci, ci, ctypes.c_double, ctypes.c_double,
+        lib.oracle_gemm_lse_mish.argtypes = [vp, vp, vp, ci, ci, ci, ci, ctypes.c_double, ctypes.c_double,
                                              ctypes.c_double, ci, ip, dp, dp]
         lib.oracle_lse_mish_rows.argtypes = [dp, ci, ci, dp, dp]
         lib.oracle_num_threads.restype = ci
@@ -169,10 +169,15 @@ def conv_point_sample(x, w, b, act: int, n_idx, oc_idx, oh_idx, ow_idx) -> np.nd
 
 
 def gemm_lse_mish(X, W, b, scale: float, cmin: float, cmax: float, rows=None):
-    """Returns (out, z) in fp64 for all rows, or for the selected ``rows``."""
-    X = np.ascontiguousarray(X, dtype=np.float32)
-    W = np.ascontiguousarray(W, dtype=np.float32)
+    """Returns (out, z) in fp64 for all rows, or for the selected ``rows``.
+
+    X and W are both float32, or both uint16 bfloat16 bit patterns (widened exactly)."""
+    X = np.ascontiguousarray(X)
+    W = np.ascontiguousarray(W)
     b = np.ascontiguousarray(b, dtype=np.float32)
+    dt = _dtype_code(X)
+    if _dtype_code(W) != dt:
+        raise TypeError("oracle: X and W must have the same dtype")
     M, K = X.shape
     N = W.shape[0]
     if W.shape != (N, K) or b.shape != (N,):
@@ -184,7 +189,7 @@ def gemm_lse_mish(X, W, b, scale: float, cmin: float, cmax: float, rows=None):
         count, rp, n = len(rows), _iptr(rows), len(rows)
     out = np.empty(n, dtype=np.float64)
     z = np.empty(n, dtype=np.float64)
-    rc = _load().oracle_gemm_lse_mish(_ptr(X), _ptr(W), _ptr(b), M, K, N, float(scale), float(cmin),
+    rc = _load().oracle_gemm_lse_mish(_ptr(X), _ptr(W), _ptr(b), dt, M, K, N, float(scale), float(cmin),
                                       float(cmax), count, rp, _dptr(out), _dptr(z))
     if rc != 0:
         raise ValueError(f"oracle_gemm_lse_mish rc={rc}")

@@ -181,10 +181,11 @@ int oracle_conv_point_sample(const void* x, const void* w, const float* b, int d
  * (l2_p22 page: the model's chain, and the two-pass max-shifted logsumexp.)
  * out[i] and (if non-NULL) z_out[i] receive row rows[i]'s results.
  */
-int oracle_gemm_lse_mish(const float* X, const float* Wt, const float* b,
+int oracle_gemm_lse_mish(const void* X, const void* Wt, const float* b, int dtype,
                          int M, int K, int N, double scale, double cmin, double cmax,
                          int count, const int* rows, double* out, double* z_out) {
     if (!X || !Wt || !b || !out || M <= 0 || K <= 0 || N <= 0 || cmin > cmax) return -1;
+    if (dtype != 0 && dtype != 1) return -1;
     int nrows = rows ? count : M;
     if (rows)
         for (int i = 0; i < count; ++i)
@@ -193,15 +194,14 @@ int oracle_gemm_lse_mish(const float* X, const float* Wt, const float* b,
 #pragma omp parallel for schedule(dynamic)
     for (int i = 0; i < nrows; ++i) {
         int m = rows ? rows[i] : i;
-        const float* xr = X + (size_t)m * K;
         double* c = (double*)malloc((size_t)N * sizeof(double));
         if (!c) { bad = 1; continue; }
         /* the scaled, clamped row and its maximum */
         double mx = -INFINITY;
         for (int j = 0; j < N; ++j) {
-            const float* wr = Wt + (size_t)j * K;
             double dot = 0.0;
-            for (int k = 0; k < K; ++k) dot += (double)xr[k] * (double)wr[k];
+            for (int k = 0; k < K; ++k)
+                dot += load_elem(X, (size_t)m * K + k, dtype) * load_elem(Wt, (size_t)j * K + k, dtype);
             c[j] = fmin(fmax(scale * (dot + (double)b[j]), cmin), cmax);
             if (c[j] > mx) mx = c[j];
         }

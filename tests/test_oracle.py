@@ -294,6 +294,27 @@ def test_gemm_lse_matches_blas_and_logsumexp(M, K, N):
         np.testing.assert_allclose(out, ro, rtol=1e-12, atol=1e-12)
 
 
+@pytest.mark.parametrize("M,K,N", [(5, 8, 9), (7, 37, 40)])
+def test_gemm_lse_bf16_inputs_match_blas_on_widened_values(M, K, N):
+    # bfloat16 is the top half of a float32: widening appends 16 zero bits
+    r = np.random.default_rng(M + K + N)
+    Xb = r.integers(0, 1 << 16, (M, K), dtype=np.uint16)
+    Wb = r.integers(0, 1 << 16, (N, K), dtype=np.uint16)
+    # keep finite, moderate values: exponent field 0x7A..0x82 (about 2^-5 .. 2^3), random signs
+    Xb = (Xb & 0x807F) | (((Xb >> 8) % 9 + 0x7A) << 7).astype(np.uint16)
+    Wb = (Wb & 0x807F) | (((Wb >> 8) % 9 + 0x7A) << 7).astype(np.uint16)
+    b = r.uniform(-0.5, 0.5, N).astype(np.float32)
+    Xf = (Xb.astype(np.uint32) << 16).view(np.float32)
+    Wf = (Wb.astype(np.uint32) << 16).view(np.float32)
+    for scale, cmin, cmax in [(4.0, -10.0, 10.0), (0.01, -1.0, 2.0)]:
+        out, z = oracle.gemm_lse_mish(Xb, Wb, b, scale, cmin, cmax)
+        ro, rz = np_gemm_lse_mish(Xf, Wf, b, scale, cmin, cmax)
+        np.testing.assert_allclose(z, rz, rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(out, ro, rtol=1e-12, atol=1e-12)
+    with pytest.raises(TypeError):
+        oracle.gemm_lse_mish(Xb, Wf, b, 4.0, -10.0, 10.0)
+
+
 def test_lse_constant_row():
     M, K, N = 3, 4, 6144
     X = np.ones((M, K), np.float32)

@@ -34,8 +34,8 @@ MUTANTS = {
     "pool_divisor_full_map": ("((double)OH * (double)OW)", "((double)H * (double)W)"),
     "lse_missing_shift": ("double z = mx + log(s);", "double z = log(s);"),
     "bias_after_scale": ("scale * (dot + (double)b[j])", "scale * dot + (double)b[j]"),
-    "gemm_w_transposed": ("dot += (double)xr[k] * (double)wr[k];",
-                          "dot += (double)xr[k] * (double)Wt[(size_t)k * N + j];"),
+    "gemm_w_transposed": ("load_elem(Wt, (size_t)j * K + k, dtype)", "load_elem(Wt, (size_t)k * N + j, dtype)"),
+    "gemm_w_read_as_float32": ("load_elem(Wt, (size_t)j * K + k, dtype)", "load_elem(Wt, (size_t)j * K + k, 0)"),
     "out_missing_z_factor": ("out[i] = z * oracle_mish(z);", "out[i] = oracle_mish(z);"),
     "act_mean_wrong_divisor": ("return s / (double)count;", "return s / (double)(count + 1);"),
     "lse_rows_scale_dropped": ("c[j] = fmin(fmax(scale * (double)r[j], cmin), cmax);",
