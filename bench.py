@@ -60,7 +60,8 @@ def gemm_flops(s) -> float:
 
 
 def gemm_bytes(s) -> float:
-    return 4.0 * (s["M"] * s["K"] + s["N"] * s["K"] + s["N"] + s["M"])
+    esz = 2 if s.get("dtype", "f32") == "bf16" else 4
+    return esz * (s["M"] * s["K"] + s["N"] * s["K"]) + 4.0 * (s["N"] + s["M"])
 
 
 def read_traffic(workload: str, kernel: str):
@@ -262,7 +263,7 @@ def main() -> int:
         to = (lambda a: torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)) if bf16 else \
             (lambda a: torch.from_numpy(a).to(dev))
         xd, wd, bd = to(x), to(w), torch.from_numpy(b).to(dev)
-        act = {0: "none", 1: "gelu", 2: "mish2"}[spec["act"]]
+        act = {0: "none", 1: "gelu", 2: "mish2", 3: "gelu_tanh"}[spec["act"]]
         out = torch.empty((spec["N"], spec["Cout"]) if spec["pool"] else
                           (spec["N"], spec["Cout"], spec["H"] - 2, spec["W"] - 2), dtype=torch.float32, device=dev)
 
@@ -273,12 +274,15 @@ def main() -> int:
                "kernel": "3x3 valid stride 1", "act": act, "pool": bool(spec["pool"]), "dtype": dtype}
     else:
         X, W, b = synth.gemm_inputs(spec)
-        xd, wd, bd = (torch.from_numpy(a).to(dev) for a in (X, W, b))
+        dtype = spec.get("dtype", "f32")
+        to = (lambda a: torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)) if dtype == "bf16" else \
+            (lambda a: torch.from_numpy(a).to(dev))
+        xd, wd, bd = to(X), to(W), torch.from_numpy(b).to(dev)
         out = torch.empty((spec["M"], 1), dtype=torch.float32, device=dev)
 
         def step():
             fc.gemm_lse_mish(xd, wd, bd, spec["scale"], spec["cmin"], spec["cmax"], out=out)
-        flops, nbytes, kernel, dtype = gemm_flops(spec), gemm_bytes(spec), "gemm_lse_partials", "f32"
+        flops, nbytes, kernel = gemm_flops(spec), gemm_bytes(spec), "gemm_lse_partials"
         cfg = {"workload": name, "M": spec["M"], "K": spec["K"], "N": spec["N"], "scale": spec["scale"],
                "clamp": [spec["cmin"], spec["cmax"]], "dtype": dtype}
 

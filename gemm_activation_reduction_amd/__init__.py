@@ -5,6 +5,7 @@ of the library. PyTorch supplies device memory and the stream. There is no CPU
 fallback -- if the library is missing, loading fails loudly.
 
 The functions with the C names (``fconv_act_pool``, ``fgemm_lse_mish``,
+``fgemm_lse_mish_bf16``, ``fact_pool``, ``fact_elementwise``, ``flse_mish_rows``,
 ``fconv_last_error``, ``fconv_release``, ``fconv_version``) take the same
 arguments as the C entry points; pointer arguments accept a tensor (its
 ``data_ptr()``) or a plain integer device address, and ``stream`` accepts a
@@ -24,12 +25,12 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libfconv.so")
 
 FCONV_OK, FCONV_EINVAL, FCONV_EUNSUPPORTED, FCONV_EHIP, FCONV_ENOMEM = 0, -1, -2, -3, -4
-ACT_NONE, ACT_GELU, ACT_MISH2 = 0, 1, 2
+ACT_NONE, ACT_GELU, ACT_MISH2, ACT_GELU_TANH = 0, 1, 2, 3
 DT_F32, DT_BF16 = 0x000, 0x100
-_ACT_NAMES = {"none": ACT_NONE, "gelu": ACT_GELU, "mish2": ACT_MISH2}
+_ACT_NAMES = {"none": ACT_NONE, "gelu": ACT_GELU, "mish2": ACT_MISH2, "gelu_tanh": ACT_GELU_TANH}
 
 # Symbols the C header declares; the loader checks that every one is exported.
-EXPORTS = ("fconv_act_pool", "fgemm_lse_mish", "fact_pool", "fact_elementwise", "flse_mish_rows",
+EXPORTS = ("fconv_act_pool", "fgemm_lse_mish", "fgemm_lse_mish_bf16", "fact_pool", "fact_elementwise", "flse_mish_rows",
            "fconv_last_error", "fconv_release", "fconv_version", "fconv_profile", "fconv_profile_read")
 
 
@@ -56,6 +57,8 @@ def load_library() -> ctypes.CDLL:
     lib.fconv_act_pool.restype = ci
     lib.fgemm_lse_mish.argtypes = [vp, vp, vp, ci, ci, ci, cf, cf, cf, vp, vp]
     lib.fgemm_lse_mish.restype = ci
+    lib.fgemm_lse_mish_bf16.argtypes = [vp, vp, vp, ci, ci, ci, cf, cf, cf, vp, vp]
+    lib.fgemm_lse_mish_bf16.restype = ci
     lib.fconv_last_error.argtypes = []
     lib.fconv_last_error.restype = ctypes.c_char_p
     lib.fconv_release.argtypes = []
@@ -138,6 +141,13 @@ def fgemm_lse_mish(x, w, b, M, K, N, scale, cmin, cmax, out, stream=None) -> Non
     _check(rc)
 
 
+def fgemm_lse_mish_bf16(x, w, b, M, K, N, scale, cmin, cmax, out, stream=None) -> None:
+    """C ``fgemm_lse_mish_bf16``: the same chain with bfloat16 x and w (fp32 accumulation)."""
+    rc = load_library().fgemm_lse_mish_bf16(_ptr(x), _ptr(w), _ptr(b), int(M), int(K), int(N), float(scale),
+                                            float(cmin), float(cmax), _ptr(out), _stream(stream))
+    _check(rc)
+
+
 def fact_pool(x, N, C, H, W, act, out, stream=None) -> None:
     """C ``fact_pool``: act then mean over each (n, c) map of a given float32 NCHW tensor."""
     _check(load_library().fact_pool(_ptr(x), int(N), int(C), int(H), int(W), int(act), _ptr(out), _stream(stream)))
@@ -182,17 +192,22 @@ def conv_act_pool(x: torch.Tensor, w: torch.Tensor, b: torch.Tensor, act="gelu",
 
 def gemm_lse_mish(x: torch.Tensor, w: torch.Tensor, b: torch.Tensor, scale: float = 4.0, cmin: float = -10.0,
                   cmax: float = 10.0, out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
-    """Tensor helper: x (M,K), w (N,K), b (N,) float32 -> out (M, 1) float32."""
+    """Tensor helper: x (M,K), w (N,K) both float32 or both bfloat16, b (N,) float32 -> out (M, 1) float32."""
+    if x.dtype != w.dtype or x.dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError("x and w must both be float32 or both bfloat16")
+    if b.dtype != torch.float32:
+        raise TypeError("b must be float32")
     for t in (x, w, b):
-        if t.dtype != torch.float32 or not t.is_cuda or not t.is_contiguous():
-            raise ValueError("tensors must be contiguous float32 device tensors")
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError("tensors must be contiguous device tensors")
     M, K = x.shape
     N = w.shape[0]
     if tuple(w.shape) != (N, K) or tuple(b.shape) != (N,):
         raise ValueError("w must be (N, K) and b (N,)")
     if out is None:
         out = torch.empty((M, 1), dtype=torch.float32, device=x.device)
-    fgemm_lse_mish(x, w, b, M, K, N, scale, cmin, cmax, out, stream)
+    call = fgemm_lse_mish_bf16 if x.dtype == torch.bfloat16 else fgemm_lse_mish
+    call(x, w, b, M, K, N, scale, cmin, cmax, out, stream)
     return out
 
 

@@ -162,6 +162,10 @@ bool overlaps(const void* a, size_t abytes, const void* b, size_t bbytes) {
     return a0 < b0 + bbytes && b0 < a0 + abytes;
 }
 
+bool known_act(int a) {
+    return a == FCONV_ACT_NONE || a == FCONV_ACT_GELU || a == FCONV_ACT_MISH2 || a == FCONV_ACT_GELU_TANH;
+}
+
 }  // namespace
 
 FCONV_API int fconv_version(void) { return 100; }
@@ -174,8 +178,7 @@ FCONV_API int fconv_act_pool(const void* x, const void* w, const float* b, int N
     if (N < 1 || Cin < 1 || Cout < 1) return fail(FCONV_EINVAL, "fconv_act_pool: N, Cin and Cout must be >= 1");
     if (H < 3 || W < 3) return fail(FCONV_EINVAL, "fconv_act_pool: H and W must be >= 3 (3x3 valid conv)");
     const int kind = act & 0xFF, dt = act & ~0xFF;
-    if (kind != FCONV_ACT_NONE && kind != FCONV_ACT_GELU && kind != FCONV_ACT_MISH2)
-        return fail(FCONV_EINVAL, "fconv_act_pool: unknown activation " + std::to_string(kind));
+    if (!known_act(kind)) return fail(FCONV_EINVAL, "fconv_act_pool: unknown activation " + std::to_string(kind));
     if (dt != FCONV_DT_F32 && dt != FCONV_DT_BF16)
         return fail(FCONV_EINVAL, "fconv_act_pool: unknown dtype bits in act");
     if (pool != 0 && pool != 1) return fail(FCONV_EINVAL, "fconv_act_pool: pool must be 0 or 1");
@@ -201,35 +204,49 @@ FCONV_API int fconv_act_pool(const void* x, const void* w, const float* b, int N
     return ok();
 }
 
-FCONV_API int fgemm_lse_mish(const float* x, const float* w, const float* b, int M, int K, int N, float scale,
-                             float cmin, float cmax, float* out, hipStream_t stream) {
-    if (!x || !w || !b || !out) return fail(FCONV_EINVAL, "fgemm_lse_mish: null pointer argument");
-    if (M < 1 || K < 1 || N < 1) return fail(FCONV_EINVAL, "fgemm_lse_mish: M, K and N must be >= 1");
-    if (!std::isfinite(scale)) return fail(FCONV_EINVAL, "fgemm_lse_mish: scale must be finite");
-    if (std::isnan(cmin) || std::isnan(cmax) || cmin > cmax)
-        return fail(FCONV_EINVAL, "fgemm_lse_mish: need cmin <= cmax (not NaN)");
-    const long long nx = (long long)M * K, nw = (long long)N * K;
-    if (nx > kMaxElems || nw > kMaxElems) return fail(FCONV_EINVAL, "fgemm_lse_mish: a tensor has 2^31 or more elements");
-    const size_t ob = (size_t)M * 4;
-    if (overlaps(out, ob, x, nx * 4) || overlaps(out, ob, w, nw * 4) || overlaps(out, ob, b, (size_t)N * 4))
-        return fail(FCONV_EINVAL, "fgemm_lse_mish: out overlaps an input");
+namespace {
 
-    const fconv::GemmPlan plan = fconv::plan_gemm(M, K, N, x, w);
-    if ((long long)plan.tilesM * plan.tilesN > 0x7FFFFFFFLL)
-        return fail(FCONV_EUNSUPPORTED, "fgemm_lse_mish: launch grid too large");
+int gemm_lse_mish_impl(const char* name, bool bf16, const void* x, const void* w, const float* b, int M, int K,
+                       int N, float scale, float cmin, float cmax, float* out, hipStream_t stream) {
+    const std::string fn(name);
+    if (!x || !w || !b || !out) return fail(FCONV_EINVAL, fn + ": null pointer argument");
+    if (M < 1 || K < 1 || N < 1) return fail(FCONV_EINVAL, fn + ": M, K and N must be >= 1");
+    if (!std::isfinite(scale)) return fail(FCONV_EINVAL, fn + ": scale must be finite");
+    if (std::isnan(cmin) || std::isnan(cmax) || cmin > cmax)
+        return fail(FCONV_EINVAL, fn + ": need cmin <= cmax (not NaN)");
+    const long long nx = (long long)M * K, nw = (long long)N * K;
+    if (nx > kMaxElems || nw > kMaxElems) return fail(FCONV_EINVAL, fn + ": a tensor has 2^31 or more elements");
+    const size_t esz = bf16 ? 2 : 4, ob = (size_t)M * 4;
+    if (overlaps(out, ob, x, nx * esz) || overlaps(out, ob, w, nw * esz) || overlaps(out, ob, b, (size_t)N * 4))
+        return fail(FCONV_EINVAL, fn + ": out overlaps an input");
+
+    const fconv::GemmPlan plan = fconv::plan_gemm(bf16, M, K, N, x, w);
+    if ((long long)plan.tilesM * plan.tilesN > 0x7FFFFFFFLL) return fail(FCONV_EUNSUPPORTED, fn + ": launch grid too large");
     void* ws = nullptr;
     int rc = get_workspace(stream, plan.workspace_bytes(), 0, &ws, nullptr);
     if (rc != FCONV_OK) return rc;
     hipError_t e = fconv::launch_gemm_lse(plan, x, w, b, scale, cmin, cmax, out, ws, stream, active_timer());
-    if (e != hipSuccess) return fail(FCONV_EHIP, std::string("fgemm_lse_mish launch: ") + hipGetErrorString(e));
+    if (e != hipSuccess) return fail(FCONV_EHIP, fn + " launch: " + hipGetErrorString(e));
     return ok();
+}
+
+}  // namespace
+
+FCONV_API int fgemm_lse_mish(const float* x, const float* w, const float* b, int M, int K, int N, float scale,
+                             float cmin, float cmax, float* out, hipStream_t stream) {
+    return gemm_lse_mish_impl("fgemm_lse_mish", false, x, w, b, M, K, N, scale, cmin, cmax, out, stream);
+}
+
+FCONV_API int fgemm_lse_mish_bf16(const void* x, const void* w, const float* b, int M, int K, int N, float scale,
+                                  float cmin, float cmax, float* out, hipStream_t stream) {
+    return gemm_lse_mish_impl("fgemm_lse_mish_bf16", true, x, w, b, M, K, N, scale, cmin, cmax, out, stream);
 }
 
 FCONV_API int fact_pool(const float* x, int N, int C, int H, int W, int act, float* out, hipStream_t stream) {
     if (!x || !out) return fail(FCONV_EINVAL, "fact_pool: null pointer argument");
     if (N < 1 || C < 1 || H < 1 || W < 1) return fail(FCONV_EINVAL, "fact_pool: N, C, H and W must be >= 1");
-    if (act != FCONV_ACT_NONE && act != FCONV_ACT_GELU && act != FCONV_ACT_MISH2)
-        return fail(FCONV_EINVAL, "fact_pool: act must be FCONV_ACT_NONE, _GELU or _MISH2 (float32 only)");
+    if (!known_act(act))
+        return fail(FCONV_EINVAL, "fact_pool: act must be FCONV_ACT_NONE, _GELU, _MISH2 or _GELU_TANH (float32 only)");
     const long long nx = (long long)N * C * H * W, nout = (long long)N * C;
     if (nx > kMaxElems) return fail(FCONV_EINVAL, "fact_pool: a tensor has 2^31 or more elements");
     if (overlaps(out, (size_t)nout * 4, x, (size_t)nx * 4)) return fail(FCONV_EINVAL, "fact_pool: out overlaps x");
@@ -242,8 +259,9 @@ FCONV_API int fact_pool(const float* x, int N, int C, int H, int W, int act, flo
 FCONV_API int fact_elementwise(const float* x, long long count, int act, float* out, hipStream_t stream) {
     if (!x || !out) return fail(FCONV_EINVAL, "fact_elementwise: null pointer argument");
     if (count < 0) return fail(FCONV_EINVAL, "fact_elementwise: count must be >= 0");
-    if (act != FCONV_ACT_NONE && act != FCONV_ACT_GELU && act != FCONV_ACT_MISH2)
-        return fail(FCONV_EINVAL, "fact_elementwise: act must be FCONV_ACT_NONE, _GELU or _MISH2 (float32 only)");
+    if (!known_act(act))
+        return fail(FCONV_EINVAL,
+                    "fact_elementwise: act must be FCONV_ACT_NONE, _GELU, _MISH2 or _GELU_TANH (float32 only)");
     if (count > (1LL << 40)) return fail(FCONV_EINVAL, "fact_elementwise: count too large");
     if (out != x && overlaps(out, (size_t)count * 4, x, (size_t)count * 4))
         return fail(FCONV_EINVAL, "fact_elementwise: out partially overlaps x (only out == x is allowed)");

@@ -527,6 +527,8 @@ hipError_t launch_act(const ConvPlan& p, const void* x, const void* wpk, const f
         case 3: return launch_typed<BF16, kActGelu, true, TL>(p, x, wpk, b, dst, stream);
         case 4: return launch_typed<BF16, kActMish2, false, TL>(p, x, wpk, b, dst, stream);
         case 5: return launch_typed<BF16, kActMish2, true, TL>(p, x, wpk, b, dst, stream);
+        case 6: return launch_typed<BF16, kActGeluTanh, false, TL>(p, x, wpk, b, dst, stream);
+        case 7: return launch_typed<BF16, kActGeluTanh, true, TL>(p, x, wpk, b, dst, stream);
         default: return hipErrorInvalidValue;
     }
 }

@@ -4,7 +4,7 @@
 
 namespace fconv {
 
-enum Act { kActNone = 0, kActGelu = 1, kActMish2 = 2 };
+enum Act { kActNone = 0, kActGelu = 1, kActMish2 = 2, kActGeluTanh = 3 };
 
 // e^v through the hardware base-2 exponential: exp(v) = 2^(v * log2 e).
 // For |v| <= 30 the relative error stays within a few 1e-6, far inside the
@@ -34,6 +34,17 @@ __device__ __forceinline__ float gelu_erf(float v) {
     return fmaf(-av, h, fmaxf(v, 0.0f));
 }
 
+// Tanh-approximation GELU, 0.5 v (1 + tanh(u)), u = sqrt(2/pi) (v + 0.044715 v^3) (the
+// l2_p67 page's approximate='tanh' form). Since 0.5 (1 + tanh(u)) = 1 / (1 + e^{-2u}), it is
+// v / (1 + 2^{v (c1 + c2 v^2)}) with c1 = -2 sqrt(2/pi) log2(e) and c2 = 0.044715 c1: three
+// VALU operations, an exponential and a reciprocal. For v << 0 the power overflows to +inf
+// and the reciprocal to 0 (the result is -0); for v >> 0 it underflows to 0 and the result
+// is v.
+__device__ __forceinline__ float gelu_tanh(float v) {
+    const float s = fmaf(v * v, -0.1029432395800235f, -2.302208198144325f);
+    return v * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(v * s));
+}
+
 // Mish(v) = v tanh(softplus(v)). With t = e^v, tanh(log(1 + t)) = q / (q + 2), q = t (t + 2):
 // one exponential and one reciprocal. t is taken at min(v, 20): for v > 20 the ratio is 1
 // to fp32 precision (2 / (q + 2) < 1e-17), so the result is v; for very negative v, q
@@ -48,6 +59,7 @@ template <int ACT>
 __device__ __forceinline__ float activate(float v) {
     if constexpr (ACT == kActGelu) return gelu_erf(v);
     else if constexpr (ACT == kActMish2) return mish_f32(mish_f32(v));
+    else if constexpr (ACT == kActGeluTanh) return gelu_tanh(v);
     else return v;
 }
 

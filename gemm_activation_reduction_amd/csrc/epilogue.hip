@@ -153,6 +153,7 @@ hipError_t launch_act_pool_map(const float* x, int N, int C, int H, int W, int a
         case kActNone: launch_pool_typed<kActNone>(vec, x, out, hw, inv, planes, stream); break;
         case kActGelu: launch_pool_typed<kActGelu>(vec, x, out, hw, inv, planes, stream); break;
         case kActMish2: launch_pool_typed<kActMish2>(vec, x, out, hw, inv, planes, stream); break;
+        case kActGeluTanh: launch_pool_typed<kActGeluTanh>(vec, x, out, hw, inv, planes, stream); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
@@ -168,6 +169,7 @@ hipError_t launch_act_elementwise(const float* x, long long count, int act, floa
         case kActNone: launch_ew_typed<kActNone>(vec, x, out, count, blocks, stream); break;
         case kActGelu: launch_ew_typed<kActGelu>(vec, x, out, count, blocks, stream); break;
         case kActMish2: launch_ew_typed<kActMish2>(vec, x, out, count, blocks, stream); break;
+        case kActGeluTanh: launch_ew_typed<kActGeluTanh>(vec, x, out, count, blocks, stream); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();

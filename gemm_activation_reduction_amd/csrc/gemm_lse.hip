@@ -4,14 +4,18 @@
 // "Kimi-K2.6 l2_p22" POPCORNBENCH page. The page materializes the GEMM output and
 // reduces it row by row; here the (M x N) product never leaves the chip:
 //   kernel 1 (gemm_lse_partials): one workgroup per BM x BN output tile computes
-//     the tile on fp32 MFMA (v_mfma_f32_16x16x4_f32, LDS double-buffered over K),
+//     the tile on MFMA (fp32: v_mfma_f32_16x16x4_f32; bf16: v_mfma_f32_16x16x32_bf16
+//     with fp32 accumulation; LDS double-buffered over K),
 //     applies bias, scale and clamp in registers and reduces each of its rows to a
 //     (max, sum exp(c - max)) pair, written to part[m][tile_n];
 //   kernel 2 (lse_merge_mish): one wave per row merges the pairs with the page's
 //     online logsumexp rule, M = max m_t, S = sum s_t e^(m_t - M), in a fixed
 //     order, then writes z * mish(z) with z = M + log S.
-// Both operands are K-contiguous (x [M][K], w [N][K]); LDS rows are BK floats of
-// K plus 4 floats of padding (conflict-free 16-byte fragment reads).
+// Both operands are K-contiguous (x [M][K], w [N][K]); an LDS row holds BK elements of
+// K (four 16-byte groups) plus one 16-byte group of padding, so the fragment reads (16
+// rows x 4 groups per wave) and the staging stores (8 rows per 8 lanes) are conflict-free.
+// Lane group g of a wave supplies the same K positions of both operands, so any order of
+// K inside a 16-byte group is a valid MFMA operand order.
 #include "device_math.h"
 #include "internal.h"
 
@@ -19,50 +23,80 @@ namespace fconv {
 namespace {
 
 typedef float f4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
-template <int BM_, int BN_, int WM_, int WN_, int BK_, int NT_>
+template <bool BF16>
+struct GElem;
+template <>
+struct GElem<false> {
+    using T = float;
+    static constexpr int PER16 = 4;  // elements per 16-byte group
+};
+template <>
+struct GElem<true> {
+    using T = unsigned short;  // bfloat16 bit patterns
+    static constexpr int PER16 = 8;
+};
+
+template <int BM_, int BN_, int WM_, int WN_, int BK_, int NT_, bool BF16_>
 struct GTile {
+    static constexpr bool BF16 = BF16_;
     static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_;
     static constexpr int NT = NT_;             // threads per workgroup
-    static constexpr int BK = BK_;             // K per LDS stage (multiple of 16)
-    static constexpr int KG = BK / 4;          // 16-byte K groups per row
-    static constexpr int PITCH = BK + 4;       // floats per LDS row (4 floats of padding)
+    static constexpr int BK = BK_;             // K elements per LDS stage (4 or more 16-byte groups)
+    static constexpr int KG = BK / GElem<BF16>::PER16;  // 16-byte K groups per row
+    static constexpr int PITCH = KG + 1;       // 16-byte units per LDS row (one of padding)
     static constexpr int MB = BM / WM / 16;   // 16-row blocks per wave
     static constexpr int NB = BN / WN / 16;   // 16-col blocks per wave
     static constexpr int IA = BM * KG, IB = BN * KG;  // float4 items per stage
     static constexpr int LA = (IA + NT - 1) / NT;      // float4 loads per thread (A)
     static constexpr int LB = (IB + NT - 1) / NT;      // float4 loads per thread (B)
     static_assert(WM * WN == NT / 64, "one wave per (row group, column group)");
+    static_assert(KG % 4 == 0, "whole MFMA K steps per stage");
 };
 
 // 256 x 192 tiles: 2048 x 6144 is exactly 256 tiles, one per CU; 8 waves of 64 x 96.
-using GTileA = GTile<256, 192, 4, 2, 16, 512>;
+using GTileF = GTile<256, 192, 4, 2, 16, 512, false>;
+using GTileH = GTile<256, 192, 4, 2, 32, 512, true>;
 
-template <bool VEC>
-__device__ __forceinline__ f4 load4(const float* __restrict__ base, int rows, int K, int row, int k) {
-    // Four consecutive K elements of one row; out-of-range elements read as zero.
+// One 16-byte group of K elements of one row (PER16 elements from k on); out-of-range
+// rows and elements read as zero.
+template <bool BF16, bool VEC>
+__device__ __forceinline__ f4 load16(const typename GElem<BF16>::T* __restrict__ base, int rows, int K, int row,
+                                     int k) {
+    constexpr int P = GElem<BF16>::PER16;
     if (row >= rows) return f4{0.f, 0.f, 0.f, 0.f};
-    const float* p = base + (long long)row * K + k;
+    const auto* p = base + (long long)row * K + k;
     if constexpr (VEC) {
-        if (k < K) return *(const f4*)p;  // K % 4 == 0: the group is all in or all out
+        if (k < K) return *(const f4*)p;  // K % P == 0: the group is all in or all out
         return f4{0.f, 0.f, 0.f, 0.f};
-    } else {
+    } else if constexpr (!BF16) {
         f4 v;
         v.x = k < K ? p[0] : 0.f;
         v.y = k + 1 < K ? p[1] : 0.f;
         v.z = k + 2 < K ? p[2] : 0.f;
         v.w = k + 3 < K ? p[3] : 0.f;
         return v;
+    } else {
+        unsigned d[4];
+#pragma unroll
+        for (int e = 0; e < P / 2; ++e) {
+            const unsigned lo = k + 2 * e < K ? p[2 * e] : 0u;
+            const unsigned hi = k + 2 * e + 1 < K ? p[2 * e + 1] : 0u;
+            d[e] = lo | (hi << 16);
+        }
+        return __builtin_bit_cast(f4, d);
     }
 }
 
 template <class TL, bool VEC>
 __global__ __launch_bounds__(TL::NT) void gemm_lse_partials(
-    const float* __restrict__ X, const float* __restrict__ Wt, const float* __restrict__ bias,
-    float2* __restrict__ part, int M, int K, int N, float scale, float cmin, float cmax, int tilesN) {
-    constexpr int BK = TL::BK, kPitch = TL::PITCH;
-    __shared__ __attribute__((aligned(16))) float As[2][TL::BM * kPitch];
-    __shared__ __attribute__((aligned(16))) float Bs[2][TL::BN * kPitch];
+    const typename GElem<TL::BF16>::T* __restrict__ X, const typename GElem<TL::BF16>::T* __restrict__ Wt,
+    const float* __restrict__ bias, float2* __restrict__ part, int M, int K, int N, float scale, float cmin,
+    float cmax, int tilesN) {
+    constexpr int BK = TL::BK, kPitch = TL::PITCH, P16 = GElem<TL::BF16>::PER16;
+    __shared__ f4 As[2][TL::BM * kPitch];
+    __shared__ f4 Bs[2][TL::BN * kPitch];
 
     const int tn = blockIdx.x % tilesN, tm = blockIdx.x / tilesN;
     const int m0 = tm * TL::BM, n0 = tn * TL::BN;
@@ -86,24 +120,26 @@ __global__ __launch_bounds__(TL::NT) void gemm_lse_partials(
 #pragma unroll
         for (int j = 0; j < TL::LA; ++j) {
             const int it = tid + j * TL::NT;
-            if (TL::IA % TL::NT == 0 || it < TL::IA) ra[j] = load4<VEC>(X, M, K, m0 + row_of(it), k0 + grp_of(it) * 4);
+            if (TL::IA % TL::NT == 0 || it < TL::IA)
+                ra[j] = load16<TL::BF16, VEC>(X, M, K, m0 + row_of(it), k0 + grp_of(it) * P16);
         }
 #pragma unroll
         for (int j = 0; j < TL::LB; ++j) {
             const int it = tid + j * TL::NT;
-            if (TL::IB % TL::NT == 0 || it < TL::IB) rb[j] = load4<VEC>(Wt, N, K, n0 + row_of(it), k0 + grp_of(it) * 4);
+            if (TL::IB % TL::NT == 0 || it < TL::IB)
+                rb[j] = load16<TL::BF16, VEC>(Wt, N, K, n0 + row_of(it), k0 + grp_of(it) * P16);
         }
     };
     auto sstore = [&](int buf) {
 #pragma unroll
         for (int j = 0; j < TL::LA; ++j) {
             const int it = tid + j * TL::NT;
-            if (TL::IA % TL::NT == 0 || it < TL::IA) *(f4*)&As[buf][row_of(it) * kPitch + grp_of(it) * 4] = ra[j];
+            if (TL::IA % TL::NT == 0 || it < TL::IA) As[buf][row_of(it) * kPitch + grp_of(it)] = ra[j];
         }
 #pragma unroll
         for (int j = 0; j < TL::LB; ++j) {
             const int it = tid + j * TL::NT;
-            if (TL::IB % TL::NT == 0 || it < TL::IB) *(f4*)&Bs[buf][row_of(it) * kPitch + grp_of(it) * 4] = rb[j];
+            if (TL::IB % TL::NT == 0 || it < TL::IB) Bs[buf][row_of(it) * kPitch + grp_of(it)] = rb[j];
         }
     };
 
@@ -115,21 +151,31 @@ __global__ __launch_bounds__(TL::NT) void gemm_lse_partials(
         const int cur = kt & 1;
         if (kt + 1 < nk) gload((kt + 1) * BK);
 #pragma unroll
-        for (int kk = 0; kk < BK / 16; ++kk) {
+        for (int kk = 0; kk < TL::KG / 4; ++kk) {
+            // lane (g, i): 16-byte group 4 kk + g of row i of each 16-row block
             f4 a[TL::MB], b[TL::NB];
 #pragma unroll
-            for (int j = 0; j < TL::MB; ++j)
-                a[j] = *(const f4*)&As[cur][(rm0 + j * 16 + i) * kPitch + kk * 16 + 4 * g];
+            for (int j = 0; j < TL::MB; ++j) a[j] = As[cur][(rm0 + j * 16 + i) * kPitch + kk * 4 + g];
 #pragma unroll
-            for (int j = 0; j < TL::NB; ++j)
-                b[j] = *(const f4*)&Bs[cur][(rn0 + j * 16 + i) * kPitch + kk * 16 + 4 * g];
-#pragma unroll
-            for (int s = 0; s < 4; ++s)
+            for (int j = 0; j < TL::NB; ++j) b[j] = Bs[cur][(rn0 + j * 16 + i) * kPitch + kk * 4 + g];
+            if constexpr (TL::BF16) {
 #pragma unroll
                 for (int jm = 0; jm < TL::MB; ++jm)
 #pragma unroll
                     for (int jn = 0; jn < TL::NB; ++jn)
-                        acc[jm][jn] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[jm][s], b[jn][s], acc[jm][jn], 0, 0, 0);
+                        acc[jm][jn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                            __builtin_bit_cast(bf16x8, a[jm]), __builtin_bit_cast(bf16x8, b[jn]), acc[jm][jn], 0, 0,
+                            0);
+            } else {
+#pragma unroll
+                for (int s = 0; s < 4; ++s)
+#pragma unroll
+                    for (int jm = 0; jm < TL::MB; ++jm)
+#pragma unroll
+                        for (int jn = 0; jn < TL::NB; ++jn)
+                            acc[jm][jn] =
+                                __builtin_amdgcn_mfma_f32_16x16x4f32(a[jm][s], b[jn][s], acc[jm][jn], 0, 0, 0);
+            }
         }
         if (kt + 1 < nk) sstore(cur ^ 1);
         __syncthreads();
@@ -215,32 +261,42 @@ __global__ __launch_bounds__(256) void lse_merge_mish(const float2* __restrict__
     }
 }
 
+template <class TL>
+hipError_t launch_partials(const GemmPlan& p, const void* x, const void* w, const float* b, float scale, float cmin,
+                           float cmax, float2* part, hipStream_t stream) {
+    using T = typename GElem<TL::BF16>::T;
+    const unsigned grid = (unsigned)(p.tilesM * p.tilesN);
+    if (p.vec)
+        hipLaunchKernelGGL((gemm_lse_partials<TL, true>), dim3(grid), dim3(TL::NT), 0, stream, (const T*)x,
+                           (const T*)w, b, part, p.M, p.K, p.N, scale, cmin, cmax, p.tilesN);
+    else
+        hipLaunchKernelGGL((gemm_lse_partials<TL, false>), dim3(grid), dim3(TL::NT), 0, stream, (const T*)x,
+                           (const T*)w, b, part, p.M, p.K, p.N, scale, cmin, cmax, p.tilesN);
+    return hipGetLastError();
+}
+
 }  // namespace
 
-GemmPlan plan_gemm(int M, int K, int N, const void* x, const void* w) {
+GemmPlan plan_gemm(bool bf16, int M, int K, int N, const void* x, const void* w) {
     GemmPlan p{};
     p.M = M; p.K = K; p.N = N;
-    p.BM = GTileA::BM; p.BN = GTileA::BN;
+    p.bf16 = bf16;
+    p.BM = bf16 ? GTileH::BM : GTileF::BM;
+    p.BN = bf16 ? GTileH::BN : GTileF::BN;
     p.tilesM = (M + p.BM - 1) / p.BM;
     p.tilesN = (N + p.BN - 1) / p.BN;
-    p.vec = (K % 4 == 0) && (((size_t)x | (size_t)w) % 16 == 0);
+    p.vec = (K % (bf16 ? 8 : 4) == 0) && (((size_t)x | (size_t)w) % 16 == 0);
     p.part_bytes = (size_t)M * p.tilesN * sizeof(float2);
     return p;
 }
 
-hipError_t launch_gemm_lse(const GemmPlan& p, const float* x, const float* w, const float* b, float scale,
+hipError_t launch_gemm_lse(const GemmPlan& p, const void* x, const void* w, const float* b, float scale,
                            float cmin, float cmax, float* out, void* workspace, hipStream_t stream,
                            KernelTimer* timer) {
     float2* part = (float2*)workspace;
-    const unsigned grid = (unsigned)(p.tilesM * p.tilesN);
     if (timer) timer->begin("gemm_lse_partials", stream);
-    if (p.vec)
-        hipLaunchKernelGGL((gemm_lse_partials<GTileA, true>), dim3(grid), dim3(GTileA::NT), 0, stream, x, w, b,
-                           part, p.M, p.K, p.N, scale, cmin, cmax, p.tilesN);
-    else
-        hipLaunchKernelGGL((gemm_lse_partials<GTileA, false>), dim3(grid), dim3(GTileA::NT), 0, stream, x, w, b,
-                           part, p.M, p.K, p.N, scale, cmin, cmax, p.tilesN);
-    hipError_t e = hipGetLastError();
+    hipError_t e = p.bf16 ? launch_partials<GTileH>(p, x, w, b, scale, cmin, cmax, part, stream)
+                          : launch_partials<GTileF>(p, x, w, b, scale, cmin, cmax, part, stream);
     if (timer) timer->end("gemm_lse_partials", stream);
     if (e != hipSuccess) return e;
     if (timer) timer->begin("lse_merge_mish", stream);

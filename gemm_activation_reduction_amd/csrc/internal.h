@@ -34,15 +34,16 @@ hipError_t launch_conv(const ConvPlan& p, const void* x, const void* w, const fl
 
 struct GemmPlan {
     int M, K, N;
+    bool bf16;               // x, w bfloat16 (else float32)
     int BM, BN;
     int tilesM, tilesN;
-    bool vec;                // K % 4 == 0 and 16-byte aligned rows: dwordx4 loads
+    bool vec;                // K a multiple of a 16-byte group, 16-byte aligned rows: dwordx4 loads
     size_t part_bytes;       // [M][tilesN] (max, sum) pairs
     size_t workspace_bytes() const { return part_bytes; }
 };
 
-GemmPlan plan_gemm(int M, int K, int N, const void* x, const void* w);
-hipError_t launch_gemm_lse(const GemmPlan& p, const float* x, const float* w, const float* b,
+GemmPlan plan_gemm(bool bf16, int M, int K, int N, const void* x, const void* w);
+hipError_t launch_gemm_lse(const GemmPlan& p, const void* x, const void* w, const float* b,
                            float scale, float cmin, float cmax, float* out, void* workspace,
                            hipStream_t stream, KernelTimer* timer);
 

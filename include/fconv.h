@@ -44,6 +44,10 @@ enum {
     FCONV_ACT_NONE = 0,   /* identity (plain conv + bias)                                 */
     FCONV_ACT_GELU = 1,   /* 0.5 v (1 + erf(v / sqrt 2)), the exact form                  */
     FCONV_ACT_MISH2 = 2,  /* mish(mish(v)), mish(v) = v tanh(log(1 + e^v))                */
+    FCONV_ACT_GELU_TANH = 3, /* 0.5 v (1 + tanh(sqrt(2/pi) (v + 0.044715 v^3))), the tanh
+                              * approximation the "Kimi-K2.6 l2_p67" page weighs against the
+                              * exact form (PyTorch's approximate='tanh'); a different function,
+                              * within 4.8e-4 of FCONV_ACT_GELU                               */
     FCONV_DT_F32 = 0x000, /* x, w float32                                                 */
     FCONV_DT_BF16 = 0x100 /* x, w bfloat16 (products exact in fp32, fp32 accumulation)    */
 };
@@ -100,11 +104,22 @@ int fgemm_lse_mish(const float* x, const float* w, const float* b,
                    float* out, hipStream_t stream);
 
 /*
+ * The same operation with bfloat16 operands: x [M][K] and w [N][K] row-major bfloat16
+ * bit patterns, b [N] and out [M] float32. Products of bfloat16 values are exact in
+ * fp32 and accumulate in fp32 (v_mfma_f32_16x16x32_bf16); bias, scale, clamp,
+ * logsumexp and z * mish(z) run in fp32. The bfloat16 variant of the l2_p22 chain
+ * (reduced-precision operands, the same epilogue). Errors as for fgemm_lse_mish.
+ */
+int fgemm_lse_mish_bf16(const void* x, const void* w, const float* b,
+                        int M, int K, int N, float scale, float cmin, float cmax,
+                        float* out, hipStream_t stream);
+
+/*
  * Epilogue-only operations over an already materialized tensor: the kernels the pages
  * write for use after a separate convolution or GEMM. All float32, all HBM-bound.
  *
  * fact_pool: out[n,c] = (1 / (H W)) * sum_{h,w} act(x[n,c,h,w]), x NCHW [N][C][H][W],
- *   out [N][C]; act = FCONV_ACT_NONE, FCONV_ACT_GELU or FCONV_ACT_MISH2 (no dtype bits).
+ *   out [N][C]; act = FCONV_ACT_NONE, _GELU, _MISH2 or _GELU_TANH (no dtype bits).
  *   Source: the GELU + AdaptiveAvgPool2d(1) kernel of the "Kimi-K2.6 l2_p67" page.
  * fact_elementwise: out[i] = act(x[i]) for 0 <= i < count; out == x (in place) is
  *   allowed, any other overlap is not. Source: the Mish -> Mish kernel of the

@@ -92,7 +92,7 @@ def bf16_bits_to_f32(u: np.ndarray) -> np.ndarray:
 # measured on: a tiny conv, three full-size convs and the GEMM + logsumexp case.
 # ----------------------------------------------------------------------------------
 
-ACT_NONE, ACT_GELU, ACT_MISH2 = 0, 1, 2
+ACT_NONE, ACT_GELU, ACT_MISH2, ACT_GELU_TANH = 0, 1, 2, 3
 
 CONV_WORKLOADS = {
     "conv_tiny": dict(cfg=1, N=2, Cin=3, H=16, W=16, Cout=8, act=ACT_GELU, pool=1, dtype="f32",
@@ -103,11 +103,18 @@ CONV_WORKLOADS = {
                                 x_dist=("normal",), w_bound=1.0 / math.sqrt(64 * 9), b_bound=0.1),
     "conv_gelu_pool_bf16": dict(cfg=4, N=16, Cin=128, H=128, W=128, Cout=256, act=ACT_GELU, pool=1, dtype="bf16",
                                 x_dist=("normal",), w_bound=1.0 / math.sqrt(128 * 9), b_bound=0.1),
+    # the same bf16 inputs (same seeds) with the tanh-approximation GELU epilogue
+    "conv_gelu_tanh_pool_bf16": dict(cfg=4, N=16, Cin=128, H=128, W=128, Cout=256, act=ACT_GELU_TANH, pool=1,
+                                     dtype="bf16", x_dist=("normal",), w_bound=1.0 / math.sqrt(128 * 9),
+                                     b_bound=0.1),
 }
 
 GEMM_WORKLOADS = {
     "gemm_lse_mish_f32": dict(cfg=5, M=2048, K=4096, N=6144, scale=4.0, cmin=-10.0, cmax=10.0,
                               w_bound=1.0 / 64, b_bound=1.0 / 64),
+    # the same draws (same seeds) with X and W rounded to bfloat16; the bias stays float32
+    "gemm_lse_mish_bf16": dict(cfg=5, M=2048, K=4096, N=6144, scale=4.0, cmin=-10.0, cmax=10.0,
+                               w_bound=1.0 / 64, b_bound=1.0 / 64, dtype="bf16"),
 }
 
 
@@ -137,12 +144,18 @@ def conv_inputs(spec: dict, seed_cfg: int | None = None):
 
 
 def gemm_inputs(spec: dict, seed_cfg: int | None = None):
-    """Returns (X (M,K), W (N,K), b (N,)) float32 host arrays for a GEMM-LSE spec."""
+    """Returns (X (M,K), W (N,K), b (N,)) host arrays for a GEMM-LSE spec.
+
+    X and W are float32, or uint16 bf16 bits when spec["dtype"] == "bf16"; b is float32.
+    """
     cfg = spec.get("cfg", 0) if seed_cfg is None else seed_cfg
     M, K, N = spec["M"], spec["K"], spec["N"]
     X = normal(seed_for(cfg, X_ID), M * K).reshape(M, K)
     W = uniform(seed_for(cfg, W_ID), N * K, -spec["w_bound"], spec["w_bound"]).reshape(N, K)
     b = uniform(seed_for(cfg, B_ID), N, -spec["b_bound"], spec["b_bound"])
+    if spec.get("dtype", "f32") == "bf16":
+        X = to_bf16_bits(X).reshape(M, K)
+        W = to_bf16_bits(W).reshape(N, K)
     return X, W, b
 
 

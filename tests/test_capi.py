@@ -70,7 +70,7 @@ def conv_err(**kw):
     (dict(x=0), "null"), (dict(w=0), "null"), (dict(b=0), "null"), (dict(out=0), "null"),
     (dict(N=0), ">= 1"), (dict(Cin=-1), ">= 1"), (dict(Cout=0), ">= 1"),
     (dict(H=2), ">= 3"), (dict(W=1), ">= 3"),
-    (dict(act=3), "unknown activation"), (dict(act=0x200 | 1), "dtype"), (dict(act=0x1000), "dtype"),
+    (dict(act=4), "unknown activation"), (dict(act=0x200 | 1), "dtype"), (dict(act=0x1000), "dtype"),
     (dict(pool=2), "pool"), (dict(pool=-1), "pool"),
     (dict(N=1 << 16, Cin=1 << 8, H=1 << 8, W=1 << 8), "2^31"),
     (dict(out=FAKE + 64), "overlaps"), (dict(out=FAKE + (1 << 30) + 100), "overlaps"),
@@ -103,6 +103,25 @@ def test_gemm_validation(kw, frag):
     assert frag in e.message
 
 
+@pytest.mark.parametrize("kw,frag", [
+    (dict(w=0), "null"), (dict(M=0), ">= 1"), (dict(scale=float("nan")), "scale"),
+    (dict(cmin=2.0, cmax=1.0), "cmin"), (dict(M=1 << 20, K=1 << 12), "2^31"),
+    (dict(out=FAKE + 8), "overlaps"),
+    # bf16 rows are 2 bytes an element: x covers 4 * 8 * 2 = 64 bytes
+    (dict(out=FAKE + 60), "overlaps"),
+])
+def test_gemm_bf16_validation(kw, frag):
+    args = dict(x=FAKE, w=FAKE + (1 << 30), b=FAKE + (2 << 30), M=4, K=8, N=16, scale=4.0, cmin=-10.0,
+                cmax=10.0, out=FAKE + (3 << 30))
+    args.update(kw)
+    with pytest.raises(fc.FconvError) as e:
+        fc.fgemm_lse_mish_bf16(args["x"], args["w"], args["b"], args["M"], args["K"], args["N"], args["scale"],
+                               args["cmin"], args["cmax"], args["out"], S0)
+    assert e.value.code == fc.FCONV_EINVAL
+    assert frag in e.value.message
+    assert "fgemm_lse_mish_bf16" in e.value.message
+
+
 def test_last_error_is_per_call():
     conv_err(N=0)
     assert ">= 1" in fc.fconv_last_error()
@@ -112,7 +131,7 @@ def test_last_error_is_per_call():
     (lambda: fc.fact_pool(0, 1, 1, 1, 1, 1, FAKE, S0), "null"),
     (lambda: fc.fact_pool(FAKE, 0, 1, 1, 1, 1, FAKE + (1 << 30), S0), ">= 1"),
     (lambda: fc.fact_pool(FAKE, 1, 1, 4, 4, 0x101, FAKE + (1 << 30), S0), "act"),
-    (lambda: fc.fact_pool(FAKE, 1, 1, 4, 4, 3, FAKE + (1 << 30), S0), "act"),
+    (lambda: fc.fact_pool(FAKE, 1, 1, 4, 4, 4, FAKE + (1 << 30), S0), "act"),
     (lambda: fc.fact_pool(FAKE, 1 << 12, 1 << 10, 1 << 5, 1 << 5, 1, FAKE + (1 << 38), S0), "2^31"),
     (lambda: fc.fact_pool(FAKE, 2, 2, 4, 4, 1, FAKE + 16, S0), "overlaps"),
     (lambda: fc.fact_elementwise(FAKE, -1, 1, FAKE + (1 << 30), S0), "count"),

@@ -43,7 +43,7 @@ SHAPES = [
 
 
 @pytest.mark.parametrize("bf16", [False, True])
-@pytest.mark.parametrize("act", [fc.ACT_NONE, fc.ACT_GELU, fc.ACT_MISH2])
+@pytest.mark.parametrize("act", [fc.ACT_NONE, fc.ACT_GELU, fc.ACT_MISH2, fc.ACT_GELU_TANH])
 @pytest.mark.parametrize("pool", [0, 1])
 @pytest.mark.parametrize("shape", SHAPES)
 def test_conv_small_shapes_full_compare(shape, pool, act, bf16):
@@ -81,7 +81,7 @@ def test_conv_zero_weights_and_constant_map():
     b = synth.uniform(77, Cout, -2.0, 2.0)
     x = synth.normal(78, N * Cin * H * W).reshape(N, Cin, H, W)
     w0 = np.zeros((Cout, Cin, 3, 3), np.float32)
-    for act in (fc.ACT_GELU, fc.ACT_MISH2):
+    for act in (fc.ACT_GELU, fc.ACT_MISH2, fc.ACT_GELU_TANH):
         expect = np.array([oracle.act(float(v), act) for v in b])
         got = run_conv(x, w0, b, act, 1)
         assert max_rel_err(got, np.broadcast_to(expect, got.shape)) <= TOL_F32
@@ -118,7 +118,8 @@ def sample_pairs(N, Cout, count, seed):
     return n, oc
 
 
-@pytest.mark.parametrize("name,count", [("conv_gelu_pool_f32", 96), ("conv_gelu_pool_bf16", 48)])
+@pytest.mark.parametrize("name,count", [("conv_gelu_pool_f32", 96), ("conv_gelu_pool_bf16", 48),
+                                        ("conv_gelu_tanh_pool_bf16", 32)])
 def test_conv_full_size_pooled_sampled(name, count):
     spec = synth.CONV_WORKLOADS[name]
     bf16 = spec["dtype"] == "bf16"

@@ -14,7 +14,7 @@ pytestmark = pytest.mark.gpu
 torch = pytest.importorskip("torch")
 import gemm_activation_reduction_amd as fc  # noqa: E402
 
-ACTS = [fc.ACT_NONE, fc.ACT_GELU, fc.ACT_MISH2]
+ACTS = [fc.ACT_NONE, fc.ACT_GELU, fc.ACT_MISH2, fc.ACT_GELU_TANH]
 
 
 def rand(seed, shape, scale=2.0):

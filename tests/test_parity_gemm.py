@@ -1,5 +1,9 @@
-"""GPU parity of fgemm_lse_mish against the fp64 CPU oracle (called through the C ABI).
-Tolerance: max |g - o| / (1 + |o|) <= 1e-4 (fp32)."""
+"""GPU parity of fgemm_lse_mish and fgemm_lse_mish_bf16 against the fp64 CPU oracle
+(called through the C ABI). Tolerance: max |g - o| / (1 + |o|) <= 1e-4.
+
+For bfloat16 operands both sides consume the same bf16 bytes (the oracle widens them
+exactly), bf16 x bf16 products are exact in fp32 and accumulate in fp32, so the fp32
+bound applies there too; it is far inside the 2e-2 allowed for bf16 inputs."""
 import math
 
 import numpy as np
@@ -16,14 +20,15 @@ import gemm_activation_reduction_amd as fc  # noqa: E402
 
 
 def run_gemm(X, W, b, scale=4.0, cmin=-10.0, cmax=10.0, stream=None):
-    out = fc.gemm_lse_mish(to_device(X), to_device(W), to_device(b), scale, cmin, cmax, stream=stream)
+    bf16 = X.dtype == np.uint16
+    out = fc.gemm_lse_mish(to_device(X, bf16), to_device(W, bf16), to_device(b), scale, cmin, cmax, stream=stream)
     torch.cuda.synchronize()
     return out.cpu().numpy()[:, 0]
 
 
-def rand_case(seed, M, K, N, wb=None):
+def rand_case(seed, M, K, N, wb=None, dtype="f32"):
     wb = wb if wb is not None else 1.0 / math.sqrt(K)
-    return synth.gemm_inputs(dict(M=M, K=K, N=N, w_bound=wb, b_bound=wb), seed_cfg=2000 + seed)
+    return synth.gemm_inputs(dict(M=M, K=K, N=N, w_bound=wb, b_bound=wb, dtype=dtype), seed_cfg=2000 + seed)
 
 
 @pytest.mark.parametrize("M,K,N", [(37, 19, 53), (1, 1, 1), (5, 4, 3), (128, 128, 128), (130, 260, 300),
@@ -35,6 +40,19 @@ def test_gemm_small_shapes(M, K, N, scale, cmin, cmax):
     ref, _ = oracle.gemm_lse_mish(X, W, b, scale, cmin, cmax)
     err = max_rel_err(got, ref)
     print(f"M={M} K={K} N={N} scale={scale} clamp=[{cmin},{cmax}] err={err:.3e}", flush=True)
+    assert err <= TOL_F32
+
+
+@pytest.mark.parametrize("M,K,N", [(37, 19, 53), (1, 1, 1), (5, 8, 3), (128, 128, 128), (130, 264, 300),
+                                   (64, 1000, 129), (257, 33, 1000), (3, 4096, 6144), (300, 72, 385)])
+@pytest.mark.parametrize("scale,cmin,cmax", [(4.0, -10.0, 10.0), (-3.0, -1e30, 1e30)])
+def test_gemm_bf16_small_shapes(M, K, N, scale, cmin, cmax):
+    # K % 8 != 0 takes the element-wise load path, K % 8 == 0 the 16-byte one
+    X, W, b = rand_case(M + K + N, M, K, N, dtype="bf16")
+    got = run_gemm(X, W, b, scale, cmin, cmax)
+    ref, _ = oracle.gemm_lse_mish(X, W, b, scale, cmin, cmax)
+    err = max_rel_err(got, ref)
+    print(f"bf16 M={M} K={K} N={N} scale={scale} clamp=[{cmin},{cmax}] err={err:.3e}", flush=True)
     assert err <= TOL_F32
 
 
@@ -74,8 +92,8 @@ def test_gemm_deterministic_and_stream():
     assert torch.equal(o1, o2) and torch.equal(o1, o3)
 
 
-def test_gemm_full_size_sampled_rows():
-    name = "gemm_lse_mish_f32"
+@pytest.mark.parametrize("name", ["gemm_lse_mish_f32", "gemm_lse_mish_bf16"])
+def test_gemm_full_size_sampled_rows(name):
     spec = synth.GEMM_WORKLOADS[name]
     X, W, b = workload_gemm_inputs(name)
     print(f"{name}: running GPU", flush=True)
