@@ -31,15 +31,21 @@ import synth  # noqa: E402
 PEAK_TFLOPS = {"f32": 157.3, "bf16": 2516.6}  # MI355X dense MFMA peaks
 HBM_GBPS = 8000.0
 DEFAULT_WORKLOAD = "conv_gelu_pool_f32"
-KERNEL_SOURCES = ["gemm_activation_reduction_amd/csrc/conv3x3.hip",
-                  "gemm_activation_reduction_amd/csrc/gemm_lse.hip",
-                  "gemm_activation_reduction_amd/csrc/epilogue.hip",
-                  "gemm_activation_reduction_amd/csrc/device_math.h"]
+_CSRC = "gemm_activation_reduction_amd/csrc/"
+# The sources each measured kernel is compiled from: a traffic summary counts only while
+# they are unchanged since its counters were taken.
+KERNEL_SOURCES = {
+    "conv3x3_fused": [_CSRC + "conv3x3.hip", _CSRC + "device_math.h"],
+    "gemm_lse_partials": [_CSRC + "gemm_lse.hip", _CSRC + "device_math.h"],
+    "act_pool_map": [_CSRC + "epilogue.hip", _CSRC + "device_math.h"],
+    "act_elementwise": [_CSRC + "epilogue.hip", _CSRC + "device_math.h"],
+    "scale_clamp_lse": [_CSRC + "epilogue.hip", _CSRC + "device_math.h"],
+}
 
 
-def source_hash() -> str:
+def source_hash(kernel: str) -> str:
     h = hashlib.sha256()
-    for rel in KERNEL_SOURCES:
+    for rel in KERNEL_SOURCES[kernel]:
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -75,7 +81,7 @@ def read_traffic(workload: str, kernel: str):
         if ":" in line and not line.startswith("#"):
             k, v = line.split(":", 1)
             vals[k.strip()] = v.strip()
-    if vals.get("source_hash") != source_hash():
+    if vals.get("source_hash") != source_hash(kernel):
         return None
     try:
         return float(vals["hbm_bytes_per_launch"])
@@ -146,6 +152,30 @@ def cpu_baseline_gemm(spec, X, W, b, got, seconds):
             "sample_max_err": float(max(errs)) if errs else None}
 
 
+def calibration_copies(args, torch, dev) -> None:
+    """Plain device copies of a known size: the reference a --pmc run scales HBM counters by."""
+    if args.calib_copy_mb > 0:
+        n = args.calib_copy_mb * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+        print(f"bench: calibration copies of {args.calib_copy_mb} MiB done", file=sys.stderr, flush=True)
+
+
+def epilogue_bytes(spec) -> float:
+    """Algorithmic bytes of one epilogue-only launch: read the tensor once, write the result."""
+    shape = spec["shape"]
+    total = int(np.prod(shape))
+    if spec["kind"] == "pool":
+        return 4.0 * (total + shape[0] * shape[1])
+    if spec["kind"] == "elementwise":
+        return 8.0 * total
+    return 4.0 * (total + shape[0])
+
+
 def bench_epilogue(args, name, spec, torch, fc, dev) -> int:
     """HBM-bound epilogue-only kernels: GB/s of algorithmic traffic against 8 TB/s."""
     print(f"bench: generating inputs for {name}", file=sys.stderr, flush=True)
@@ -160,16 +190,16 @@ def bench_epilogue(args, name, spec, torch, fc, dev) -> int:
     if kind == "pool":
         N, C, H, W = shape
         out = torch.empty((N, C), dtype=torch.float32, device=dev)
-        nbytes, kernel = 4.0 * (total + N * C), "act_pool_map"
+        nbytes, kernel = epilogue_bytes(spec), "act_pool_map"
         step = lambda: fc.fact_pool(xd, N, C, H, W, spec["act"], out)  # noqa: E731
     elif kind == "elementwise":
         out = torch.empty_like(xd)
-        nbytes, kernel = 8.0 * total, "act_elementwise"
+        nbytes, kernel = epilogue_bytes(spec), "act_elementwise"
         step = lambda: fc.fact_elementwise(xd, total, spec["act"], out)  # noqa: E731
     else:
         M, N = shape
         out = torch.empty((M, 1), dtype=torch.float32, device=dev)
-        nbytes, kernel = 4.0 * (total + M), "scale_clamp_lse"
+        nbytes, kernel = epilogue_bytes(spec), "scale_clamp_lse"
         step = lambda: fc.flse_mish_rows(xd, M, N, spec["scale"], spec["cmin"], spec["cmax"], out)  # noqa: E731
     for _ in range(args.warmup):
         step()
@@ -191,6 +221,7 @@ def bench_epilogue(args, name, spec, torch, fc, dev) -> int:
     achieved = nbytes / (kernel_ms * 1e-3) / 1e9
     print(f"bench: {ms_per_step:.4f} ms/step, {kernel} {kernel_ms:.4f} ms/launch, {achieved:.1f} GB/s",
           file=sys.stderr, flush=True)
+    calibration_copies(args, torch, dev)
     cpu = None
     if args.cpu_seconds > 0:
         import oracle
@@ -323,14 +354,7 @@ def main() -> int:
           f"over {klaunches} launches, {achieved:.2f} TFLOP/s, {nbytes / (kernel_ms * 1e-3) / 1e9:.1f} GB/s algorithmic",
           file=sys.stderr, flush=True)
 
-    if args.calib_copy_mb > 0:
-        n = args.calib_copy_mb * (1 << 20) // 4
-        src = torch.ones(n, dtype=torch.float32, device=dev)
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        print(f"bench: calibration copies of {args.calib_copy_mb} MiB done", file=sys.stderr, flush=True)
+    calibration_copies(args, torch, dev)
 
     cpu = None
     if args.cpu_seconds > 0:

@@ -56,8 +56,8 @@ struct GTile {
 };
 
 // 256 x 192 tiles: 2048 x 6144 is exactly 256 tiles, one per CU; 8 waves of 64 x 96.
-using GTileF = GTile<256, 192, 4, 2, 16, 512, false>;
-using GTileH = GTile<256, 192, 4, 2, 32, 512, true>;
+using GTileF = GTile<256, 192, 4, 2, 32, 512, false>;
+using GTileH = GTile<256, 192, 4, 2, 64, 512, true>;
 
 // One 16-byte group of K elements of one row (PER16 elements from k on); out-of-range
 // rows and elements read as zero.
@@ -112,10 +112,12 @@ __global__ __launch_bounds__(TL::NT) void gemm_lse_partials(
         for (int b = 0; b < TL::NB; ++b) acc[a][b] = f4{0.f, 0.f, 0.f, 0.f};
 
     f4 ra[TL::LA], rb[TL::LB];
-    // Item it -> (row, 16-byte K group): each 16 * KG items are 16 rows x KG groups with
-    // rows fastest, so the LDS stores of eight consecutive lanes hit distinct bank slots.
-    auto row_of = [](int it) { return (it & 15) + 16 * (it / (16 * TL::KG)); };
-    auto grp_of = [](int it) { return (it >> 4) % TL::KG; };
+    // Item it -> (row, 16-byte K group). With 8 or more groups a row's stage is whole
+    // 128-byte lines: groups go fastest, so eight lanes read one line and store to eight
+    // consecutive LDS slots. With 4 groups (64 bytes) each 16 * KG items are 16 rows x KG
+    // groups with rows fastest, so eight consecutive lanes still hit distinct bank slots.
+    auto row_of = [](int it) { return TL::KG >= 8 ? it / TL::KG : (it & 15) + 16 * (it / (16 * TL::KG)); };
+    auto grp_of = [](int it) { return TL::KG >= 8 ? it % TL::KG : (it >> 4) % TL::KG; };
     auto gload = [&](int k0) {
 #pragma unroll
         for (int j = 0; j < TL::LA; ++j) {
