@@ -59,6 +59,11 @@ def _load():
         lib.oracle_conv_pool_sample.argtypes = [vp, vp, vp, ci, ci, ci, ci, ci, ci, ci, ci, ip, ip, dp]
         lib.oracle_conv_point_sample.argtypes = [vp, vp, vp, ci, ci, ci, ci, ci, ci, ci, ci,
                                                  ip, ip, ip, ip, dp]
+        lib.oracle_conv2d_act_pool.argtypes = [vp, vp, vp, ci, ci, ci, ci, ci, ci, ci, ci, ci, ci, ci, dp]
+        lib.oracle_conv2d_pool_sample.argtypes = [vp, vp, vp, ci, ci, ci, ci, ci, ci, ci, ci, ci, ci,
+                                                  ci, ip, ip, dp]
+        lib.oracle_conv2d_point_sample.argtypes = [vp, vp, vp, ci, ci, ci, ci, ci, ci, ci, ci, ci, ci,
+                                                   ci, ip, ip, ip, ip, dp]
         lib.oracle_gemm_lse_mish.argtypes = [vp, vp, vp, ci, ci, ci, ci, ctypes.c_double, ctypes.c_double,
                                              ctypes.c_double, ci, ip, dp, dp]
         lib.oracle_lse_mish_rows.argtypes = [dp, ci, ci, dp, dp]
@@ -117,7 +122,7 @@ def num_threads() -> int:
     return int(_load().oracle_num_threads())
 
 
-def _conv_args(x, w, b):
+def _conv_args(x, w, b, K=3):
     x = np.ascontiguousarray(x)
     w = np.ascontiguousarray(w)
     b = np.ascontiguousarray(b, dtype=np.float32)
@@ -126,7 +131,7 @@ def _conv_args(x, w, b):
         raise TypeError("oracle: x and w must share a dtype")
     N, Cin, H, W = x.shape
     Cout = w.shape[0]
-    if w.shape != (Cout, Cin, 3, 3) or b.shape != (Cout,):
+    if w.shape != (Cout, Cin, K, K) or b.shape != (Cout,):
         raise ValueError("oracle: shape mismatch")
     return x, w, b, code, N, Cin, H, W, Cout
 
@@ -165,6 +170,55 @@ def conv_point_sample(x, w, b, act: int, n_idx, oc_idx, oh_idx, ow_idx) -> np.nd
                                           int(act), len(idx[0]), *[_iptr(a) for a in idx], _dptr(out))
     if rc != 0:
         raise ValueError(f"oracle_conv_point_sample rc={rc}")
+    return out
+
+
+def conv2d_out_size(H: int, W: int, K: int, stride: int, pad: int) -> tuple[int, int]:
+    """(OH, OW) of a K x K convolution with the given stride and zero padding."""
+    return (H + 2 * pad - K) // stride + 1, (W + 2 * pad - K) // stride + 1
+
+
+def conv2d_act_pool(x, w, b, stride: int, pad: int, act: int, pool: int) -> np.ndarray:
+    """General-geometry fused conv in fp64 (square K x K kernel from w's shape, stride, zero
+    padding): (N, Cout) if pool else (N, Cout, OH, OW)."""
+    K = int(np.shape(w)[-1])
+    x, w, b, code, N, Cin, H, W, Cout = _conv_args(x, w, b, K)
+    OH, OW = conv2d_out_size(H, W, K, stride, pad)
+    shape = (N, Cout) if pool else (N, Cout, OH, OW)
+    out = np.empty(shape, dtype=np.float64)
+    rc = _load().oracle_conv2d_act_pool(_ptr(x), _ptr(w), _ptr(b), code, N, Cin, H, W, Cout, K, int(stride),
+                                        int(pad), int(act), int(pool), _dptr(out))
+    if rc != 0:
+        raise ValueError(f"oracle_conv2d_act_pool rc={rc}")
+    return out
+
+
+def conv2d_pool_sample(x, w, b, stride: int, pad: int, act: int, n_idx, oc_idx) -> np.ndarray:
+    """Pooled fp64 general-geometry outputs at the selected (n, oc) pairs."""
+    K = int(np.shape(w)[-1])
+    x, w, b, code, N, Cin, H, W, Cout = _conv_args(x, w, b, K)
+    n_idx = np.ascontiguousarray(n_idx, dtype=np.int32)
+    oc_idx = np.ascontiguousarray(oc_idx, dtype=np.int32)
+    out = np.empty(len(n_idx), dtype=np.float64)
+    rc = _load().oracle_conv2d_pool_sample(_ptr(x), _ptr(w), _ptr(b), code, N, Cin, H, W, Cout, K, int(stride),
+                                           int(pad), int(act), len(n_idx), _iptr(n_idx), _iptr(oc_idx),
+                                           _dptr(out))
+    if rc != 0:
+        raise ValueError(f"oracle_conv2d_pool_sample rc={rc}")
+    return out
+
+
+def conv2d_point_sample(x, w, b, stride: int, pad: int, act: int, n_idx, oc_idx, oh_idx, ow_idx) -> np.ndarray:
+    """Activated fp64 general-geometry outputs at the selected (n, oc, oh, ow) points."""
+    K = int(np.shape(w)[-1])
+    x, w, b, code, N, Cin, H, W, Cout = _conv_args(x, w, b, K)
+    idx = [np.ascontiguousarray(a, dtype=np.int32) for a in (n_idx, oc_idx, oh_idx, ow_idx)]
+    out = np.empty(len(idx[0]), dtype=np.float64)
+    rc = _load().oracle_conv2d_point_sample(_ptr(x), _ptr(w), _ptr(b), code, N, Cin, H, W, Cout, K, int(stride),
+                                            int(pad), int(act), len(idx[0]), *[_iptr(a) for a in idx],
+                                            _dptr(out))
+    if rc != 0:
+        raise ValueError(f"oracle_conv2d_point_sample rc={rc}")
     return out
 
 

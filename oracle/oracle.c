@@ -173,6 +173,110 @@ int oracle_conv_point_sample(const void* x, const void* w, const float* b, int d
     return 0;
 }
 
+/* ---------------------------------------------------------------------------------
+ * General geometry: a square K x K kernel, stride S, zero padding P on all four sides
+ * (nn.Conv2d's kernel_size / stride / padding). The pages fix K = 3, S = 1, P = 0; the
+ * same direct sum with those three parameters opened up:
+ *   pre[n,oc,oh,ow] = b[oc] + sum_{ic,kh,kw} w[oc,ic,kh,kw] * xp[n,ic,oh*S+kh-P,ow*S+kw-P]
+ * where xp reads zero outside 0 <= row < H, 0 <= col < W, and
+ *   OH = (H + 2P - K) / S + 1,  OW = (W + 2P - K) / S + 1   (integer division).
+ * --------------------------------------------------------------------------------- */
+static double conv2d_pre(const void* x, const void* w, const float* b, int dtype, int Cin, int H, int W,
+                         int K, int S, int P, int n, int oc, int oh, int ow) {
+    double acc = 0.0;
+    for (int ic = 0; ic < Cin; ++ic) {
+        for (int kh = 0; kh < K; ++kh) {
+            int ih = oh * S + kh - P;
+            if (ih < 0 || ih >= H) continue; /* zero padding */
+            for (int kw = 0; kw < K; ++kw) {
+                int iw = ow * S + kw - P;
+                if (iw < 0 || iw >= W) continue;
+                size_t xi = (((size_t)n * Cin + ic) * H + ih) * W + iw;
+                size_t wi = (((size_t)oc * Cin + ic) * K + kh) * K + kw;
+                acc += load_elem(w, wi, dtype) * load_elem(x, xi, dtype);
+            }
+        }
+    }
+    return acc + (double)b[oc];
+}
+
+static int conv2d_geometry(int H, int W, int K, int S, int P, int* OH, int* OW) {
+    if (K < 1 || S < 1 || P < 0 || H + 2 * P < K || W + 2 * P < K) return -1;
+    *OH = (H + 2 * P - K) / S + 1;
+    *OW = (W + 2 * P - K) / S + 1;
+    return 0;
+}
+
+/* Mean over the OH x OW output map of act(pre[n,oc,.,.]). */
+static double conv2d_pool_one(const void* x, const void* w, const float* b, int dtype, int Cin, int H, int W,
+                              int K, int S, int P, int n, int oc, int act) {
+    int OH = 0, OW = 0;
+    conv2d_geometry(H, W, K, S, P, &OH, &OW); /* validated by every caller */
+    double s = 0.0;
+    for (int oh = 0; oh < OH; ++oh)
+        for (int ow = 0; ow < OW; ++ow)
+            s += oracle_act(conv2d_pre(x, w, b, dtype, Cin, H, W, K, S, P, n, oc, oh, ow), act);
+    return s / ((double)OH * (double)OW);
+}
+
+/* Full general-geometry conv: out [N][Cout] (pool = 1) or [N][Cout][OH][OW] (pool = 0). */
+int oracle_conv2d_act_pool(const void* x, const void* w, const float* b, int dtype,
+                           int N, int Cin, int H, int W, int Cout, int K, int S, int P,
+                           int act, int pool, double* out) {
+    int OH, OW;
+    if (!x || !w || !b || !out || N <= 0 || Cin <= 0 || Cout <= 0 || H <= 0 || W <= 0) return -1;
+    if (conv2d_geometry(H, W, K, S, P, &OH, &OW)) return -1;
+    long long NC = (long long)N * Cout;
+    if (pool) {
+#pragma omp parallel for schedule(dynamic)
+        for (long long t = 0; t < NC; ++t)
+            out[t] = conv2d_pool_one(x, w, b, dtype, Cin, H, W, K, S, P, (int)(t / Cout), (int)(t % Cout), act);
+    } else {
+        long long rows = NC * OH;
+#pragma omp parallel for schedule(dynamic, 16)
+        for (long long t = 0; t < rows; ++t) {
+            int oh = (int)(t % OH);
+            long long nc = t / OH;
+            int n = (int)(nc / Cout), oc = (int)(nc % Cout);
+            double* o = out + (size_t)t * OW;
+            for (int ow = 0; ow < OW; ++ow)
+                o[ow] = oracle_act(conv2d_pre(x, w, b, dtype, Cin, H, W, K, S, P, n, oc, oh, ow), act);
+        }
+    }
+    return 0;
+}
+
+/* Pooled general-geometry outputs for `count` selected (n, oc) pairs. */
+int oracle_conv2d_pool_sample(const void* x, const void* w, const float* b, int dtype,
+                              int N, int Cin, int H, int W, int Cout, int K, int S, int P, int act,
+                              int count, const int* n_idx, const int* oc_idx, double* out) {
+    int OH, OW;
+    if (!x || !w || !b || !out || conv2d_geometry(H, W, K, S, P, &OH, &OW)) return -1;
+    for (int i = 0; i < count; ++i)
+        if (n_idx[i] < 0 || n_idx[i] >= N || oc_idx[i] < 0 || oc_idx[i] >= Cout) return -1;
+#pragma omp parallel for schedule(dynamic)
+    for (int i = 0; i < count; ++i)
+        out[i] = conv2d_pool_one(x, w, b, dtype, Cin, H, W, K, S, P, n_idx[i], oc_idx[i], act);
+    return 0;
+}
+
+/* Activated general-geometry outputs at `count` selected (n, oc, oh, ow) points. */
+int oracle_conv2d_point_sample(const void* x, const void* w, const float* b, int dtype,
+                               int N, int Cin, int H, int W, int Cout, int K, int S, int P, int act,
+                               int count, const int* n_idx, const int* oc_idx,
+                               const int* oh_idx, const int* ow_idx, double* out) {
+    int OH, OW;
+    if (!x || !w || !b || !out || conv2d_geometry(H, W, K, S, P, &OH, &OW)) return -1;
+    for (int i = 0; i < count; ++i)
+        if (n_idx[i] < 0 || n_idx[i] >= N || oc_idx[i] < 0 || oc_idx[i] >= Cout ||
+            oh_idx[i] < 0 || oh_idx[i] >= OH || ow_idx[i] < 0 || ow_idx[i] >= OW) return -1;
+#pragma omp parallel for schedule(static)
+    for (int i = 0; i < count; ++i)
+        out[i] = oracle_act(conv2d_pre(x, w, b, dtype, Cin, H, W, K, S, P, n_idx[i], oc_idx[i],
+                                       oh_idx[i], ow_idx[i]), act);
+    return 0;
+}
+
 /*
  * GEMM + logsumexp + z*mish(z) for `count` selected rows (rows == NULL: all M rows).
  *   y[m,j] = scale * (sum_k X[m,k] W[j,k] + b[j]);  c = min(max(y, cmin), cmax)

@@ -385,6 +385,92 @@ def test_gemm_bias_is_added_before_scale():
     assert z[0] == pytest.approx(2.0 + math.log(3), rel=1e-15)
 
 
+# ------------------------------------------------------------------ general geometry (K x K, stride, padding)
+def np_conv2d(x, w, b, stride, pad):
+    """Zero-pad, then take strided K x K windows (independent of the oracle's loops)."""
+    x = np.pad(np.asarray(x, np.float64), ((0, 0), (0, 0), (pad, pad), (pad, pad)))
+    K = w.shape[-1]
+    win = np.lib.stride_tricks.sliding_window_view(x, (K, K), axis=(2, 3))[:, :, ::stride, ::stride]
+    return np.einsum("ncyxij,ocij->noyx", win, np.asarray(w, np.float64)) + np.asarray(b, np.float64)[None, :, None, None]
+
+
+GEOMS = [(1, 1, 0), (1, 2, 0), (3, 1, 1), (3, 2, 1), (3, 2, 0), (5, 1, 2), (5, 2, 2), (5, 1, 0), (3, 1, 2)]
+
+
+@pytest.mark.parametrize("K,S,P", GEOMS)
+@pytest.mark.parametrize("act", [oracle.ACT_NONE, oracle.ACT_GELU, oracle.ACT_MISH2, oracle.ACT_GELU_TANH])
+def test_conv2d_matches_torch_and_bruteforce(K, S, P, act):
+    import torch
+    r = np.random.default_rng(K * 100 + S * 10 + P + act)
+    x = r.uniform(-1, 1, (2, 3, 11, 9)).astype(np.float32)
+    w = r.uniform(-0.3, 0.3, (4, 3, K, K)).astype(np.float32)
+    b = r.uniform(-0.5, 0.5, 4).astype(np.float32)
+    pre = torch.nn.functional.conv2d(torch.from_numpy(x).double(), torch.from_numpy(w).double(),
+                                     torch.from_numpy(b).double(), stride=S, padding=P).numpy()
+    np.testing.assert_allclose(np_conv2d(x, w, b, S, P), pre, rtol=1e-12, atol=1e-13)
+    ref = np_act(pre, act)
+    full = oracle.conv2d_act_pool(x, w, b, S, P, act, 0)
+    assert full.shape == ref.shape == (2, 4) + oracle.conv2d_out_size(11, 9, K, S, P)
+    np.testing.assert_allclose(full, ref, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(oracle.conv2d_act_pool(x, w, b, S, P, act, 1), ref.mean(axis=(2, 3)),
+                               rtol=1e-12, atol=1e-13)
+
+
+def test_conv2d_reduces_to_the_3x3_valid_oracle():
+    x, w, b = rng_case(77, 2, 5, 10, 12, 6)
+    for act in (oracle.ACT_GELU, oracle.ACT_MISH2):
+        for pool in (0, 1):
+            np.testing.assert_array_equal(oracle.conv2d_act_pool(x, w, b, 1, 0, act, pool),
+                                          oracle.conv_act_pool(x, w, b, act, pool))
+
+
+def test_conv2d_1x1_is_a_channel_matmul():
+    r = np.random.default_rng(3)
+    x = r.normal(size=(2, 6, 5, 7)).astype(np.float32)
+    w = r.normal(size=(3, 6, 1, 1)).astype(np.float32)
+    b = r.normal(size=3).astype(np.float32)
+    expect = np.einsum("nchw,oc->nohw", x.astype(np.float64), w[:, :, 0, 0].astype(np.float64)) + b[None, :, None, None]
+    np.testing.assert_allclose(oracle.conv2d_act_pool(x, w, b, 1, 0, oracle.ACT_NONE, 0), expect, rtol=1e-13)
+    # stride 2 keeps every other row and column
+    np.testing.assert_allclose(oracle.conv2d_act_pool(x, w, b, 2, 0, oracle.ACT_NONE, 0), expect[:, :, ::2, ::2],
+                               rtol=1e-13)
+
+
+def test_conv2d_zero_padding_counts_taps_at_the_border():
+    # x = 1 everywhere, w = 1 everywhere, b = 0, 3x3 with padding 1: an output sums the
+    # in-range taps times Cin -- 4 at a corner, 6 on an edge, 9 inside
+    Cin = 2
+    x = np.ones((1, Cin, 5, 6), np.float32)
+    w = np.ones((1, Cin, 3, 3), np.float32)
+    out = oracle.conv2d_act_pool(x, w, np.zeros(1, np.float32), 1, 1, oracle.ACT_NONE, 0)[0, 0]
+    assert out.shape == (5, 6)
+    assert out[0, 0] == out[0, -1] == out[-1, 0] == out[-1, -1] == 4 * Cin
+    assert out[0, 2] == out[2, 0] == out[-1, 3] == out[3, -1] == 6 * Cin
+    assert np.all(out[1:-1, 1:-1] == 9 * Cin)
+    # zero weights: act(b) everywhere, padded border included; the mean divides by OH * OW
+    b = np.array([0.7], np.float32)
+    for act in (oracle.ACT_GELU, oracle.ACT_MISH2):
+        full = oracle.conv2d_act_pool(x, 0 * w, b, 2, 2, act, 0)
+        assert full.shape == (1, 1, 4, 4)
+        np.testing.assert_allclose(full, oracle.act(float(b[0]), act), rtol=1e-15)
+        assert oracle.conv2d_act_pool(x, 0 * w, b, 2, 2, act, 1)[0, 0] == pytest.approx(oracle.act(float(b[0]), act),
+                                                                                       rel=1e-15)
+
+
+def test_conv2d_samples_match_full():
+    x, w, b = rng_case(5, 3, 4, 13, 12, 5)
+    w5 = np.random.default_rng(1).uniform(-0.2, 0.2, (5, 4, 5, 5)).astype(np.float32)
+    full = oracle.conv2d_act_pool(x, w5, b, 2, 2, oracle.ACT_GELU, 0)
+    pooled = oracle.conv2d_act_pool(x, w5, b, 2, 2, oracle.ACT_GELU, 1)
+    n, oc = np.array([0, 2, 1]), np.array([4, 0, 2])
+    np.testing.assert_array_equal(oracle.conv2d_pool_sample(x, w5, b, 2, 2, oracle.ACT_GELU, n, oc), pooled[n, oc])
+    oh, ow = np.array([0, 6, 3]), np.array([5, 0, 2])
+    np.testing.assert_array_equal(oracle.conv2d_point_sample(x, w5, b, 2, 2, oracle.ACT_GELU, n, oc, oh, ow),
+                                  full[n, oc, oh, ow])
+    with pytest.raises(ValueError):
+        oracle.conv2d_point_sample(x, w5, b, 2, 2, oracle.ACT_GELU, [0], [0], [7], [0])  # OH = 7
+
+
 # ------------------------------------------------------------------ epilogue-only operations
 @pytest.mark.parametrize("act", [oracle.ACT_NONE, oracle.ACT_GELU, oracle.ACT_MISH2, oracle.ACT_GELU_TANH])
 def test_act_pool_map_matches_numpy(act):

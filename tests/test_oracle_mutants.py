@@ -29,6 +29,11 @@ MUTANTS = {
     "gelu_tanh_no_cubic": ("(v + 0.044715 * v * v * v)", "(v)"),
     "gelu_tanh_wrong_constant": ("0.044715", "0.04715"),
     "gelu_tanh_half_dropped": ("return 0.5 * v * (1.0 + tanh(", "return v * (1.0 + tanh("),
+    "conv2d_stride_ignored": ("int ih = oh * S + kh - P;", "int ih = oh + kh - P;"),
+    "conv2d_padding_sign": ("int iw = ow * S + kw - P;", "int iw = ow * S + kw + P;"),
+    "conv2d_padding_clamped": ("if (ih < 0 || ih >= H) continue; /* zero padding */",
+                               "if (ih < 0) ih = 0; if (ih >= H) ih = H - 1;"),
+    "conv2d_out_size": ("*OH = (H + 2 * P - K) / S + 1;", "*OH = (H + 2 * P - K) / S;"),
     "softplus_wrong_sign": ("log1p(exp(-fabs(v)))", "log1p(exp(fabs(v)))"),
     "single_mish": ("return oracle_mish(oracle_mish(v));", "return oracle_mish(v);"),
     "pool_divisor_full_map": ("((double)OH * (double)OW)", "((double)H * (double)W)"),
