@@ -35,7 +35,8 @@ _CSRC = "gemm_activation_reduction_amd/csrc/"
 # The sources each measured kernel is compiled from: a traffic summary counts only while
 # they are unchanged since its counters were taken.
 KERNEL_SOURCES = {
-    "conv3x3_fused": [_CSRC + "conv3x3.hip", _CSRC + "device_math.h"],
+    "conv3x3_fused": [_CSRC + "conv3x3.hip", _CSRC + "conv_common.h", _CSRC + "device_math.h"],
+    "conv_general_fused": [_CSRC + "conv_general.hip", _CSRC + "conv_common.h", _CSRC + "device_math.h"],
     "gemm_lse_partials": [_CSRC + "gemm_lse.hip", _CSRC + "device_math.h"],
     "act_pool_map": [_CSRC + "epilogue.hip", _CSRC + "device_math.h"],
     "act_elementwise": [_CSRC + "epilogue.hip", _CSRC + "device_math.h"],
@@ -52,13 +53,17 @@ def source_hash(kernel: str) -> str:
 
 
 def conv_flops(s) -> float:
-    return 2.0 * s["N"] * s["Cout"] * (s["H"] - 2) * (s["W"] - 2) * s["Cin"] * 9
+    K = synth.conv_geometry(s)[0]
+    OH, OW = synth.conv_out_size(s)
+    return 2.0 * s["N"] * s["Cout"] * OH * OW * s["Cin"] * K * K
 
 
 def conv_bytes(s) -> float:
     esz = 2 if s["dtype"] == "bf16" else 4
-    out = s["N"] * s["Cout"] * (1 if s["pool"] else (s["H"] - 2) * (s["W"] - 2))
-    return esz * (s["N"] * s["Cin"] * s["H"] * s["W"] + s["Cout"] * s["Cin"] * 9) + 4 * s["Cout"] + 4 * out
+    K = synth.conv_geometry(s)[0]
+    OH, OW = synth.conv_out_size(s)
+    out = s["N"] * s["Cout"] * (1 if s["pool"] else OH * OW)
+    return esz * (s["N"] * s["Cin"] * s["H"] * s["W"] + s["Cout"] * s["Cin"] * K * K) + 4 * s["Cout"] + 4 * out
 
 
 def gemm_flops(s) -> float:
@@ -89,6 +94,22 @@ def read_traffic(workload: str, kernel: str):
         return None
 
 
+def oracle_pool_sample(spec, x, w, b, n, oc):
+    import oracle
+    K, S, P = synth.conv_geometry(spec)
+    if (K, S, P) == (3, 1, 0):
+        return oracle.conv_pool_sample(x, w, b, spec["act"], n, oc)
+    return oracle.conv2d_pool_sample(x, w, b, S, P, spec["act"], n, oc)
+
+
+def oracle_point_sample(spec, x, w, b, n, oc, oh, ow):
+    import oracle
+    K, S, P = synth.conv_geometry(spec)
+    if (K, S, P) == (3, 1, 0):
+        return oracle.conv_point_sample(x, w, b, spec["act"], n, oc, oh, ow)
+    return oracle.conv2d_point_sample(x, w, b, S, P, spec["act"], n, oc, oh, ow)
+
+
 def cpu_baseline_conv(spec, x, w, b, got_pool, seconds):
     """fp64 oracle on a bounded sample of (n, oc) maps of the same workload."""
     import oracle
@@ -100,7 +121,7 @@ def cpu_baseline_conv(spec, x, w, b, got_pool, seconds):
     while done < len(order) and time.perf_counter() - t0 < seconds:
         sel = order[done:done + batch]
         n, oc = sel // Cout, sel % Cout
-        ref = oracle.conv_pool_sample(x, w, b, spec["act"], n, oc)
+        ref = oracle_pool_sample(spec, x, w, b, n, oc)
         if got_pool is not None:
             errs.append(np.max(np.abs(got_pool[n, oc] - ref) / (1 + np.abs(ref))))
         done += len(sel)
@@ -114,14 +135,15 @@ def cpu_baseline_conv(spec, x, w, b, got_pool, seconds):
 def cpu_baseline_conv_points(spec, x, w, b, out_dev, seconds):
     import oracle
     import torch
-    N, Cout, OH, OW = spec["N"], spec["Cout"], spec["H"] - 2, spec["W"] - 2
+    N, Cout = spec["N"], spec["Cout"]
+    OH, OW = synth.conv_out_size(spec)
     r = np.random.default_rng(2)
-    flops_per_pt = 2.0 * spec["Cin"] * 9
+    flops_per_pt = 2.0 * spec["Cin"] * synth.conv_geometry(spec)[0] ** 2
     done, t0, errs, batch = 0, time.perf_counter(), [], 200000
     while time.perf_counter() - t0 < seconds:
         n, oc = r.integers(0, N, batch), r.integers(0, Cout, batch)
         oh, ow = r.integers(0, OH, batch), r.integers(0, OW, batch)
-        ref = oracle.conv_point_sample(x, w, b, spec["act"], n, oc, oh, ow)
+        ref = oracle_point_sample(spec, x, w, b, n, oc, oh, ow)
         idx = [torch.from_numpy(a.astype(np.int64)).to(out_dev.device) for a in (n, oc, oh, ow)]
         got = out_dev[idx[0], idx[1], idx[2], idx[3]].cpu().numpy()
         errs.append(np.max(np.abs(got - ref) / (1 + np.abs(ref))))
@@ -295,14 +317,17 @@ def main() -> int:
             (lambda a: torch.from_numpy(a).to(dev))
         xd, wd, bd = to(x), to(w), torch.from_numpy(b).to(dev)
         act = {0: "none", 1: "gelu", 2: "mish2", 3: "gelu_tanh"}[spec["act"]]
+        OH, OW = synth.conv_out_size(spec)
+        K, S, P = synth.conv_geometry(spec)
         out = torch.empty((spec["N"], spec["Cout"]) if spec["pool"] else
-                          (spec["N"], spec["Cout"], spec["H"] - 2, spec["W"] - 2), dtype=torch.float32, device=dev)
+                          (spec["N"], spec["Cout"], OH, OW), dtype=torch.float32, device=dev)
 
         def step():
-            fc.conv_act_pool(xd, wd, bd, act=act, pool=bool(spec["pool"]), out=out)
-        flops, nbytes, kernel, dtype = conv_flops(spec), conv_bytes(spec), "conv3x3_fused", spec["dtype"]
+            fc.conv2d_act_pool(xd, wd, bd, stride=S, pad=P, act=act, pool=bool(spec["pool"]), out=out)
+        kernel = "conv3x3_fused" if (K, S, P) == (3, 1, 0) else "conv_general_fused"
+        flops, nbytes, dtype = conv_flops(spec), conv_bytes(spec), spec["dtype"]
         cfg = {"workload": name, "x": [spec["N"], spec["Cin"], spec["H"], spec["W"]], "cout": spec["Cout"],
-               "kernel": "3x3 valid stride 1", "act": act, "pool": bool(spec["pool"]), "dtype": dtype}
+               "kernel": f"{K}x{K} stride {S} pad {P}", "act": act, "pool": bool(spec["pool"]), "dtype": dtype}
     else:
         X, W, b = synth.gemm_inputs(spec)
         dtype = spec.get("dtype", "f32")

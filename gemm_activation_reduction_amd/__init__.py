@@ -5,7 +5,7 @@ of the library. PyTorch supplies device memory and the stream. There is no CPU
 fallback -- if the library is missing, loading fails loudly.
 
 The functions with the C names (``fconv_act_pool``, ``fgemm_lse_mish``,
-``fgemm_lse_mish_bf16``, ``fact_pool``, ``fact_elementwise``, ``flse_mish_rows``,
+``fconv2d_act_pool``, ``fgemm_lse_mish_bf16``, ``fact_pool``, ``fact_elementwise``, ``flse_mish_rows``,
 ``fconv_last_error``, ``fconv_release``, ``fconv_version``) take the same
 arguments as the C entry points; pointer arguments accept a tensor (its
 ``data_ptr()``) or a plain integer device address, and ``stream`` accepts a
@@ -30,7 +30,7 @@ DT_F32, DT_BF16 = 0x000, 0x100
 _ACT_NAMES = {"none": ACT_NONE, "gelu": ACT_GELU, "mish2": ACT_MISH2, "gelu_tanh": ACT_GELU_TANH}
 
 # Symbols the C header declares; the loader checks that every one is exported.
-EXPORTS = ("fconv_act_pool", "fgemm_lse_mish", "fgemm_lse_mish_bf16", "fact_pool", "fact_elementwise", "flse_mish_rows",
+EXPORTS = ("fconv_act_pool", "fconv2d_act_pool", "fgemm_lse_mish", "fgemm_lse_mish_bf16", "fact_pool", "fact_elementwise", "flse_mish_rows",
            "fconv_last_error", "fconv_release", "fconv_version", "fconv_profile", "fconv_profile_read")
 
 
@@ -55,6 +55,8 @@ def load_library() -> ctypes.CDLL:
     vp, ci, cf = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
     lib.fconv_act_pool.argtypes = [vp, vp, vp, ci, ci, ci, ci, ci, ci, ci, vp, vp]
     lib.fconv_act_pool.restype = ci
+    lib.fconv2d_act_pool.argtypes = [vp, vp, vp, ci, ci, ci, ci, ci, ci, ci, ci, ci, ci, vp, vp]
+    lib.fconv2d_act_pool.restype = ci
     lib.fgemm_lse_mish.argtypes = [vp, vp, vp, ci, ci, ci, cf, cf, cf, vp, vp]
     lib.fgemm_lse_mish.restype = ci
     lib.fgemm_lse_mish_bf16.argtypes = [vp, vp, vp, ci, ci, ci, cf, cf, cf, vp, vp]
@@ -134,6 +136,14 @@ def fconv_act_pool(x, w, b, N, Cin, H, W, Cout, act, pool, out, stream=None) -> 
     _check(rc)
 
 
+def fconv2d_act_pool(x, w, b, N, Cin, H, W, Cout, K, stride, pad, act, pool, out, stream=None) -> None:
+    """C ``fconv2d_act_pool``: K x K conv with stride and zero padding + bias + activation (+ mean)."""
+    rc = load_library().fconv2d_act_pool(_ptr(x), _ptr(w), _ptr(b), int(N), int(Cin), int(H), int(W), int(Cout),
+                                         int(K), int(stride), int(pad), int(act), int(pool), _ptr(out),
+                                         _stream(stream))
+    _check(rc)
+
+
 def fgemm_lse_mish(x, w, b, M, K, N, scale, cmin, cmax, out, stream=None) -> None:
     """C ``fgemm_lse_mish``: Linear -> scale -> clamp -> row logsumexp -> z * mish(z)."""
     rc = load_library().fgemm_lse_mish(_ptr(x), _ptr(w), _ptr(b), int(M), int(K), int(N), float(scale),
@@ -187,6 +197,29 @@ def conv_act_pool(x: torch.Tensor, w: torch.Tensor, b: torch.Tensor, act="gelu",
         out = torch.empty(shape, dtype=torch.float32, device=x.device)
     code = _act_code(act) | (DT_BF16 if x.dtype == torch.bfloat16 else DT_F32)
     fconv_act_pool(x, w, b, N, Cin, H, W, Cout, code, 1 if pool else 0, out, stream)
+    return out
+
+
+def conv2d_act_pool(x: torch.Tensor, w: torch.Tensor, b: torch.Tensor, stride: int = 1, pad: int = 0, act="gelu",
+                    pool: bool = True, out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """Tensor helper: x (N,Cin,H,W), w (Cout,Cin,K,K) float32 or bfloat16, b (Cout,) float32."""
+    if x.dtype != w.dtype or x.dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError("x and w must both be float32 or both bfloat16")
+    if b.dtype != torch.float32:
+        raise TypeError("b must be float32")
+    for t in (x, w, b):
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError("tensors must be contiguous device tensors")
+    N, Cin, H, W = x.shape
+    Cout, K = w.shape[0], w.shape[-1]
+    if tuple(w.shape) != (Cout, Cin, K, K) or tuple(b.shape) != (Cout,):
+        raise ValueError("w must be (Cout, Cin, K, K) and b (Cout,)")
+    OH, OW = (H + 2 * pad - K) // stride + 1, (W + 2 * pad - K) // stride + 1
+    shape = (N, Cout) if pool else (N, Cout, OH, OW)
+    if out is None:
+        out = torch.empty(shape, dtype=torch.float32, device=x.device)
+    code = _act_code(act) | (DT_BF16 if x.dtype == torch.bfloat16 else DT_F32)
+    fconv2d_act_pool(x, w, b, N, Cin, H, W, Cout, K, stride, pad, code, 1 if pool else 0, out, stream)
     return out
 
 

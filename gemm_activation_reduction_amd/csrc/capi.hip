@@ -172,36 +172,62 @@ FCONV_API int fconv_version(void) { return 100; }
 
 FCONV_API const char* fconv_last_error(void) { return g_last_error.c_str(); }
 
-FCONV_API int fconv_act_pool(const void* x, const void* w, const float* b, int N, int Cin, int H, int W,
-                             int Cout, int act, int pool, float* out, hipStream_t stream) {
-    if (!x || !w || !b || !out) return fail(FCONV_EINVAL, "fconv_act_pool: null pointer argument");
-    if (N < 1 || Cin < 1 || Cout < 1) return fail(FCONV_EINVAL, "fconv_act_pool: N, Cin and Cout must be >= 1");
-    if (H < 3 || W < 3) return fail(FCONV_EINVAL, "fconv_act_pool: H and W must be >= 3 (3x3 valid conv)");
+namespace {
+
+int conv_impl(const char* name, const void* x, const void* w, const float* b, int N, int Cin, int H, int W,
+              int Cout, int K, int stride, int pad, int act, int pool, float* out, hipStream_t stream) {
+    const std::string fn(name);
+    if (!x || !w || !b || !out) return fail(FCONV_EINVAL, fn + ": null pointer argument");
+    if (N < 1 || Cin < 1 || Cout < 1) return fail(FCONV_EINVAL, fn + ": N, Cin and Cout must be >= 1");
+    if (K < 1 || stride < 1 || pad < 0) return fail(FCONV_EINVAL, fn + ": need K >= 1, stride >= 1, pad >= 0");
+    if (H < 1 || W < 1 || H + 2 * pad < K || W + 2 * pad < K)
+        return fail(FCONV_EINVAL, fn + ": the padded input is smaller than the kernel (H and W must be >= 3 for "
+                                       "a 3x3 valid conv)");
     const int kind = act & 0xFF, dt = act & ~0xFF;
-    if (!known_act(kind)) return fail(FCONV_EINVAL, "fconv_act_pool: unknown activation " + std::to_string(kind));
-    if (dt != FCONV_DT_F32 && dt != FCONV_DT_BF16)
-        return fail(FCONV_EINVAL, "fconv_act_pool: unknown dtype bits in act");
-    if (pool != 0 && pool != 1) return fail(FCONV_EINVAL, "fconv_act_pool: pool must be 0 or 1");
-    const long long nx = (long long)N * Cin * H * W, nw = (long long)Cout * Cin * 9;
-    const long long nout = pool ? (long long)N * Cout : (long long)N * Cout * (H - 2) * (W - 2);
+    if (!known_act(kind)) return fail(FCONV_EINVAL, fn + ": unknown activation " + std::to_string(kind));
+    if (dt != FCONV_DT_F32 && dt != FCONV_DT_BF16) return fail(FCONV_EINVAL, fn + ": unknown dtype bits in act");
+    if (pool != 0 && pool != 1) return fail(FCONV_EINVAL, fn + ": pool must be 0 or 1");
+    const bool fast = K == 3 && stride == 1 && pad == 0;
+    if (!fast && !fconv::conv_general_supported(K, stride))
+        return fail(FCONV_EUNSUPPORTED, fn + ": kernel size must be 1, 3 or 5 and stride 1 or 2");
+    if (pad >= K) return fail(FCONV_EUNSUPPORTED, fn + ": padding must be smaller than the kernel size");
+    const long long OH = (H + 2LL * pad - K) / stride + 1, OW = (W + 2LL * pad - K) / stride + 1;
+    const long long nx = (long long)N * Cin * H * W, nw = (long long)Cout * Cin * K * K;
+    const long long nout = pool ? (long long)N * Cout : (long long)N * Cout * OH * OW;
     if (nx > kMaxElems || nw > kMaxElems || nout > kMaxElems)
-        return fail(FCONV_EINVAL, "fconv_act_pool: a tensor has 2^31 or more elements");
+        return fail(FCONV_EINVAL, fn + ": a tensor has 2^31 or more elements");
     const size_t esz = dt == FCONV_DT_BF16 ? 2 : 4;
     const size_t ob = (size_t)nout * 4;
     if (overlaps(out, ob, x, nx * esz) || overlaps(out, ob, w, nw * esz) || overlaps(out, ob, b, (size_t)Cout * 4))
-        return fail(FCONV_EINVAL, "fconv_act_pool: out overlaps an input");
+        return fail(FCONV_EINVAL, fn + ": out overlaps an input");
 
-    const fconv::ConvPlan plan = fconv::plan_conv(dt == FCONV_DT_BF16, kind, pool, N, Cin, H, W, Cout);
-    if (plan.grid() > 0x7FFFFFFFLL) return fail(FCONV_EUNSUPPORTED, "fconv_act_pool: launch grid too large");
+    const bool bf16 = dt == FCONV_DT_BF16;
+    const fconv::ConvPlan plan = fast ? fconv::plan_conv(bf16, kind, pool, N, Cin, H, W, Cout)
+                                      : fconv::plan_conv_general(bf16, kind, pool, N, Cin, H, W, Cout, K, stride, pad);
+    if (plan.grid() > 0x7FFFFFFFLL) return fail(FCONV_EUNSUPPORTED, fn + ": launch grid too large");
     // The kernels address one image of x, and the repacked weights, with 32-bit byte offsets.
     if ((long long)Cin * H * W * (long long)esz > 0x7FFF0000LL || (long long)plan.wpack_bytes > 0x7FFF0000LL)
-        return fail(FCONV_EUNSUPPORTED, "fconv_act_pool: one image (or the weights) exceeds 2 GiB");
+        return fail(FCONV_EUNSUPPORTED, fn + ": one image (or the weights) exceeds 2 GiB");
     void* ws = nullptr;
     int rc = get_workspace(stream, plan.workspace_bytes(), 0, &ws, nullptr);
     if (rc != FCONV_OK) return rc;
-    hipError_t e = fconv::launch_conv(plan, x, w, b, out, ws, stream, active_timer());
-    if (e != hipSuccess) return fail(FCONV_EHIP, std::string("fconv_act_pool launch: ") + hipGetErrorString(e));
+    hipError_t e = fast ? fconv::launch_conv(plan, x, w, b, out, ws, stream, active_timer())
+                        : fconv::launch_conv_general(plan, x, w, b, out, ws, stream, active_timer());
+    if (e != hipSuccess) return fail(FCONV_EHIP, fn + " launch: " + hipGetErrorString(e));
     return ok();
+}
+
+}  // namespace
+
+FCONV_API int fconv_act_pool(const void* x, const void* w, const float* b, int N, int Cin, int H, int W,
+                             int Cout, int act, int pool, float* out, hipStream_t stream) {
+    return conv_impl("fconv_act_pool", x, w, b, N, Cin, H, W, Cout, 3, 1, 0, act, pool, out, stream);
+}
+
+FCONV_API int fconv2d_act_pool(const void* x, const void* w, const float* b, int N, int Cin, int H, int W,
+                               int Cout, int K, int stride, int pad, int act, int pool, float* out,
+                               hipStream_t stream) {
+    return conv_impl("fconv2d_act_pool", x, w, b, N, Cin, H, W, Cout, K, stride, pad, act, pool, out, stream);
 }
 
 namespace {

@@ -27,6 +27,7 @@
 #include <cstdint>
 #include <type_traits>
 
+#include "conv_common.h"
 #include "device_math.h"
 #include "internal.h"
 
@@ -40,17 +41,6 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 constexpr int kThreads = 256;
 constexpr int kRow = 80;  // bytes per LDS row (64 data + 16 pad)
 
-template <bool BF16> struct Elem;
-template <> struct Elem<false> {
-    using T = float;
-    static constexpr int CK = 16;   // channels per K chunk
-    static constexpr int EPG = 4;   // elements per 16-byte group
-};
-template <> struct Elem<true> {
-    using T = unsigned short;       // bfloat16 bit pattern
-    static constexpr int CK = 32;
-    static constexpr int EPG = 8;
-};
 
 template <int TH_, int TW_, int BN_, int WP_, int WO_, int MINW_, int PFD_, int NT_>
 struct Tile {
@@ -80,28 +70,6 @@ using TileA = Tile<8, 32, 64, 4, 1, 2, 1, 256>;
 // workgroup per CU, or 32-oc tiles with 3 workgroups per CU, were both slower).
 using TileB = Tile<8, 32, 64, 4, 1, 2, 1, 256>;
 
-// Repack OIHW weights to [chunk][tap][CoutPad][CK], zero-filling channels >= Cin and
-// oc >= Cout, so a workgroup's slice for one chunk is 9 contiguous [BN][CK] blocks.
-template <bool BF16>
-__global__ void pack_weights(const typename Elem<BF16>::T* __restrict__ w,
-                             typename Elem<BF16>::T* __restrict__ wp,
-                             int Cin, int Cout, int CoutPad, long long total) {
-    using T = typename Elem<BF16>::T;
-    constexpr int CK = Elem<BF16>::CK;
-    for (long long idx = (long long)blockIdx.x * blockDim.x + threadIdx.x; idx < total;
-         idx += (long long)gridDim.x * blockDim.x) {
-        int c = (int)(idx % CK);
-        long long r = idx / CK;
-        int oc = (int)(r % CoutPad);
-        r /= CoutPad;
-        int tap = (int)(r % 9);
-        int chunk = (int)(r / 9);
-        int ic = chunk * CK + c;
-        T v = 0;
-        if (oc < Cout && ic < Cin) v = w[((long long)oc * Cin + ic) * 9 + tap];
-        wp[idx] = v;
-    }
-}
 
 // ---------------------------------------------------------------------------------
 // Staging of one K chunk (CK input channels) into LDS, split into a global-load half
@@ -110,15 +78,6 @@ __global__ void pack_weights(const typename Elem<BF16>::T* __restrict__ w,
 // of a thread's loads are in flight together.
 // ---------------------------------------------------------------------------------
 
-// All staging loads are raw buffer loads: the resource covers one image of x (or the
-// repacked weights), offsets are 32-bit, and an offset past the end (kOOB) reads as zero
-// without touching memory -- so padding channels, rows below the image and columns
-// right of it are zero-filled without branches around the loads.
-constexpr int kOOB = 0x7FFFFFF0;
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, unsigned bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
-}
 
 // Halo tile, vector path (W a multiple of the 16-byte pixel group, 16-byte aligned x):
 // each item loads one 16-byte run of VW pixels from each of the EPG channels of one
@@ -272,13 +231,6 @@ struct WeightStage {
     }
 };
 
-// Workgroups are dispatched to the 8 XCDs round-robin by blockIdx.x; renumber them so
-// each XCD receives a contiguous range of logical tiles (neighbouring spatial tiles and
-// all oc tiles of a spatial tile share that XCD's L2).
-__device__ __forceinline__ int xcd_contiguous_index(int b, int G) {
-    const int xcd = b & 7, idx = b >> 3, per = G >> 3, rem = G & 7;
-    return xcd * per + (xcd < rem ? xcd : rem) + idx;
-}
 
 template <bool BF16, bool VEC, int ACT, bool POOL, class TL>
 __global__ __launch_bounds__(TL::NT) __attribute__((amdgpu_waves_per_eu(TL::MINW))) void conv3x3_fused(
@@ -481,26 +433,6 @@ __global__ __launch_bounds__(TL::NT) __attribute__((amdgpu_waves_per_eu(TL::MINW
     }
 }
 
-// Pool level 2: out[n][oc] = (sum over tiles t of part[n][t][oc]) / area, summed in a
-// fixed order. One workgroup per (image, 64 output channels); its four waves take four
-// contiguous tile ranges (lanes = consecutive channels, so every load is one 256-byte
-// row), and the four range sums are added in range order through LDS.
-__global__ __launch_bounds__(256) void pool_finalize(const float* __restrict__ part, float* __restrict__ out,
-                                                     int Cout, int nTiles, float area) {
-    __shared__ float red[4][64];
-    const int n = blockIdx.x, lane = threadIdx.x & 63, sl = threadIdx.x >> 6;
-    const int oc = blockIdx.y * 64 + lane;
-    const int per = (nTiles + 3) / 4, t0 = sl * per, t1 = min(nTiles, t0 + per);
-    float s = 0.0f;
-    if (oc < Cout) {
-        const float* p = part + (long long)n * nTiles * Cout + oc;
-#pragma unroll 8
-        for (int t = t0; t < t1; ++t) s += p[(long long)t * Cout];
-    }
-    red[sl][lane] = s;
-    __syncthreads();
-    if (sl == 0 && oc < Cout) out[(long long)n * Cout + oc] = ((red[0][lane] + red[1][lane]) + red[2][lane] + red[3][lane]) / area;
-}
 
 template <bool BF16, int ACT, bool POOL, class TL>
 hipError_t launch_typed(const ConvPlan& p, const void* x, const void* wpk, const float* b,
@@ -540,7 +472,7 @@ ConvPlan plan_conv(bool bf16, int act, int pool, int N, int Cin, int H, int W, i
     p.bf16 = bf16; p.act = act; p.pool = pool;
     p.N = N; p.Cin = Cin; p.H = H; p.W = W; p.Cout = Cout;
     p.OH = H - 2; p.OW = W - 2;
-    p.tile_cfg = 0;
+    p.KS = 3; p.stride = 1; p.pad = 0; p.general = false;
     p.tile_cfg = bf16 ? 1 : 0;
     p.TH = bf16 ? TileB::TH : TileA::TH;
     p.TW = bf16 ? TileB::TW : TileA::TW;
@@ -567,10 +499,10 @@ hipError_t launch_conv(const ConvPlan& p, const void* x, const void* w, const fl
     if (timer) timer->begin("pack_weights", stream);
     if (p.bf16)
         hipLaunchKernelGGL(pack_weights<true>, dim3(pblocks), dim3(256), 0, stream,
-                           (const unsigned short*)w, (unsigned short*)wpk, p.Cin, p.Cout, p.CoutPad, total);
+                           (const unsigned short*)w, (unsigned short*)wpk, p.Cin, p.Cout, p.CoutPad, 9, total);
     else
         hipLaunchKernelGGL(pack_weights<false>, dim3(pblocks), dim3(256), 0, stream, (const float*)w,
-                           (float*)wpk, p.Cin, p.Cout, p.CoutPad, total);
+                           (float*)wpk, p.Cin, p.Cout, p.CoutPad, 9, total);
     hipError_t e = hipGetLastError();
     if (timer) timer->end("pack_weights", stream);
     if (e != hipSuccess) return e;

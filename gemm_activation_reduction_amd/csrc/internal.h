@@ -19,10 +19,12 @@ struct ConvPlan {
     int act, pool;
     int N, Cin, H, W, Cout;
     int OH, OW;
+    int KS, stride, pad;     // kernel size, stride, zero padding (3, 1, 0 on the 3x3 valid path)
+    bool general;            // planned for the general-geometry kernel
     int tile_cfg;            // index of the tile configuration used
     int TH, TW, BN, CK;      // output tile rows/cols, oc per workgroup, channels per K chunk
     int tilesH, tilesW, ocTiles, nChunk, CoutPad;
-    size_t wpack_bytes;      // repacked weights [nChunk][9][CoutPad][CK]
+    size_t wpack_bytes;      // repacked weights [nChunk][KS * KS][CoutPad][CK]
     size_t part_bytes;       // pool partials [N][tilesH * tilesW][Cout] fp32
     size_t workspace_bytes() const { return wpack_bytes + part_bytes; }
     long long grid() const { return (long long)N * tilesH * tilesW * ocTiles; }
@@ -31,6 +33,13 @@ struct ConvPlan {
 ConvPlan plan_conv(bool bf16, int act, int pool, int N, int Cin, int H, int W, int Cout);
 hipError_t launch_conv(const ConvPlan& p, const void* x, const void* w, const float* b,
                        float* out, void* workspace, hipStream_t stream, KernelTimer* timer);
+
+// General geometry: K x K kernel (K in {1, 3, 5}), stride 1 or 2, zero padding.
+bool conv_general_supported(int K, int stride);
+ConvPlan plan_conv_general(bool bf16, int act, int pool, int N, int Cin, int H, int W, int Cout, int K, int stride,
+                           int pad);
+hipError_t launch_conv_general(const ConvPlan& p, const void* x, const void* w, const float* b, float* out,
+                               void* workspace, hipStream_t stream, KernelTimer* timer);
 
 struct GemmPlan {
     int M, K, N;

@@ -80,6 +80,28 @@ int fconv_act_pool(const void* x, const void* w, const float* b,
                    int act, int pool, float* out, hipStream_t stream);
 
 /*
+ * The same fused operation for a K x K kernel with stride and zero padding (nn.Conv2d's
+ * kernel_size, stride and padding; the pages fix K = 3, stride 1, padding 0):
+ *   pre[n,oc,oh,ow] = b[oc] + sum_{ic, kh<K, kw<K} w[oc,ic,kh,kw] * xp[n, ic, oh*stride + kh - pad,
+ *                                                                     ow*stride + kw - pad]
+ * where xp is x with zeros outside 0 <= row < H, 0 <= col < W, and
+ *   OH = (H + 2 pad - K) / stride + 1,   OW = (W + 2 pad - K) / stride + 1.
+ * pool == 1 averages act(pre) over the OH x OW map (padded borders included, as
+ * AdaptiveAvgPool2d(1) does on the conv output).
+ *
+ *   w    [Cout][Cin][K][K] OIHW, same dtype as x; all other arguments as fconv_act_pool,
+ *        out [N][Cout] or [N][Cout][OH][OW].
+ *
+ * Supported: K in {1, 3, 5}, stride in {1, 2}, 0 <= pad < K. K = 3, stride 1, pad 0 runs
+ * the same kernel as fconv_act_pool. Returns FCONV_EINVAL for the fconv_act_pool errors,
+ * K < 1, stride < 1, pad < 0 or a padded input smaller than the kernel;
+ * FCONV_EUNSUPPORTED for another K or stride, or pad >= K.
+ */
+int fconv2d_act_pool(const void* x, const void* w, const float* b,
+                     int N, int Cin, int H, int W, int Cout, int K, int stride, int pad,
+                     int act, int pool, float* out, hipStream_t stream);
+
+/*
  * Fused GEMM + scale + clamp + row logsumexp + z*mish(z).
  *
  *   y[m,j] = scale * (sum_k x[m,k] * w[j,k] + b[j])
@@ -154,7 +176,7 @@ int fconv_release(void);
  * fconv_profile_read(kernel, &ms, &launches) waits for the recorded events and returns
  * the summed event time in milliseconds and the number of launches of `kernel` since
  * the last fconv_profile() call. Kernel names: "pack_weights", "conv3x3_fused",
- * "pool_finalize", "gemm_lse_partials", "lse_merge_mish", "act_pool_map", "act_elementwise",
+ * "conv_general_fused", "pool_finalize", "gemm_lse_partials", "lse_merge_mish", "act_pool_map", "act_elementwise",
  * "scale_clamp_lse". Unknown names read as zero.
  * Returns FCONV_EINVAL for a null argument, FCONV_EHIP if an event wait fails.
  */

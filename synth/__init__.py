@@ -94,6 +94,16 @@ def bf16_bits_to_f32(u: np.ndarray) -> np.ndarray:
 
 ACT_NONE, ACT_GELU, ACT_MISH2, ACT_GELU_TANH = 0, 1, 2, 3
 
+def conv_geometry(spec: dict) -> tuple[int, int, int]:
+    """(kernel size, stride, padding) of a conv workload (3, 1, 0 unless stated)."""
+    return spec.get("K", 3), spec.get("stride", 1), spec.get("pad", 0)
+
+
+def conv_out_size(spec: dict) -> tuple[int, int]:
+    K, S, P = conv_geometry(spec)
+    return (spec["H"] + 2 * P - K) // S + 1, (spec["W"] + 2 * P - K) // S + 1
+
+
 CONV_WORKLOADS = {
     "conv_tiny": dict(cfg=1, N=2, Cin=3, H=16, W=16, Cout=8, act=ACT_GELU, pool=1, dtype="f32",
                       x_dist=("uniform", -1.0, 1.0), w_bound=1.0 / math.sqrt(27), b_bound=1.0 / math.sqrt(27)),
@@ -103,6 +113,17 @@ CONV_WORKLOADS = {
                                 x_dist=("normal",), w_bound=1.0 / math.sqrt(64 * 9), b_bound=0.1),
     "conv_gelu_pool_bf16": dict(cfg=4, N=16, Cin=128, H=128, W=128, Cout=256, act=ACT_GELU, pool=1, dtype="bf16",
                                 x_dist=("normal",), w_bound=1.0 / math.sqrt(128 * 9), b_bound=0.1),
+    # general geometry (kernel size K, stride, zero padding): the pages fix K = 3, stride 1,
+    # padding 0; these open the three parameters up on the same operator chains
+    "conv5x5_same_gelu_pool_f32": dict(cfg=9, N=64, Cin=16, H=224, W=224, Cout=64, K=5, stride=1, pad=2,
+                                       act=ACT_GELU, pool=1, dtype="f32", x_dist=("normal",),
+                                       w_bound=1.0 / math.sqrt(16 * 25), b_bound=0.1),
+    "conv3x3_s2_gelu_pool_bf16": dict(cfg=10, N=16, Cin=128, H=128, W=128, Cout=256, K=3, stride=2, pad=1,
+                                      act=ACT_GELU, pool=1, dtype="bf16", x_dist=("normal",),
+                                      w_bound=1.0 / math.sqrt(128 * 9), b_bound=0.1),
+    "conv1x1_mish2_full_f32": dict(cfg=11, N=32, Cin=64, H=192, W=192, Cout=128, K=1, stride=1, pad=0,
+                                   act=ACT_MISH2, pool=0, dtype="f32", x_dist=("normal",),
+                                   w_bound=1.0 / math.sqrt(64), b_bound=0.1),
     # the same bf16 inputs (same seeds) with the tanh-approximation GELU epilogue
     "conv_gelu_tanh_pool_bf16": dict(cfg=4, N=16, Cin=128, H=128, W=128, Cout=256, act=ACT_GELU_TANH, pool=1,
                                      dtype="bf16", x_dist=("normal",), w_bound=1.0 / math.sqrt(128 * 9),
@@ -121,12 +142,14 @@ GEMM_WORKLOADS = {
 def conv_inputs(spec: dict, seed_cfg: int | None = None):
     """Returns (x, w, b) host arrays for a conv workload spec.
 
-    x: (N, Cin, H, W), w: (Cout, Cin, 3, 3) as float32 or uint16 bf16 bits; b: (Cout,) float32.
+    x: (N, Cin, H, W), w: (Cout, Cin, K, K) (K = spec.get("K", 3)) as float32 or uint16 bf16 bits;
+    b: (Cout,) float32.
     ``seed_cfg`` overrides the config number used for seeding (for ad-hoc shapes).
     """
     cfg = spec.get("cfg", 0) if seed_cfg is None else seed_cfg
     N, Cin, H, W, Cout = spec["N"], spec["Cin"], spec["H"], spec["W"], spec["Cout"]
-    nx, nw = N * Cin * H * W, Cout * Cin * 9
+    K = spec.get("K", 3)
+    nx, nw = N * Cin * H * W, Cout * Cin * K * K
     dist = spec.get("x_dist", ("normal",))
     if dist[0] == "normal":
         x = normal(seed_for(cfg, X_ID), nx)
@@ -136,7 +159,7 @@ def conv_inputs(spec: dict, seed_cfg: int | None = None):
     w = uniform(seed_for(cfg, W_ID), nw, -wb, wb)
     b = uniform(seed_for(cfg, B_ID), Cout, -bb, bb)
     x = x.reshape(N, Cin, H, W)
-    w = w.reshape(Cout, Cin, 3, 3)
+    w = w.reshape(Cout, Cin, K, K)
     if spec.get("dtype", "f32") == "bf16":
         x = to_bf16_bits(x).reshape(x.shape)
         w = to_bf16_bits(w).reshape(w.shape)

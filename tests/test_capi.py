@@ -122,6 +122,35 @@ def test_gemm_bf16_validation(kw, frag):
     assert "fgemm_lse_mish_bf16" in e.value.message
 
 
+def conv2d_err(**kw):
+    args = dict(x=FAKE, w=FAKE + (1 << 30), b=FAKE + (2 << 30), N=2, Cin=3, H=16, W=16, Cout=8, K=5, stride=2,
+                pad=2, act=fc.ACT_GELU, pool=1, out=FAKE + (3 << 30))
+    args.update(kw)
+    with pytest.raises(fc.FconvError) as e:
+        fc.fconv2d_act_pool(args["x"], args["w"], args["b"], args["N"], args["Cin"], args["H"], args["W"],
+                            args["Cout"], args["K"], args["stride"], args["pad"], args["act"], args["pool"],
+                            args["out"], S0)
+    return e.value
+
+
+@pytest.mark.parametrize("kw,code,frag", [
+    (dict(K=0), fc.FCONV_EINVAL, "K >= 1"), (dict(stride=0), fc.FCONV_EINVAL, "stride >= 1"),
+    (dict(pad=-1), fc.FCONV_EINVAL, "pad >= 0"), (dict(H=1, pad=1), fc.FCONV_EINVAL, "smaller than the kernel"),
+    (dict(W=2, pad=0), fc.FCONV_EINVAL, "smaller than the kernel"),
+    (dict(K=7, pad=3), fc.FCONV_EUNSUPPORTED, "kernel size"), (dict(K=2, pad=0), fc.FCONV_EUNSUPPORTED, "kernel size"),
+    (dict(stride=3), fc.FCONV_EUNSUPPORTED, "stride"), (dict(pad=5), fc.FCONV_EUNSUPPORTED, "padding"),
+    (dict(act=9), fc.FCONV_EINVAL, "unknown activation"), (dict(x=0), fc.FCONV_EINVAL, "null"),
+    (dict(out=FAKE + 64), fc.FCONV_EINVAL, "overlaps"),
+    # w is Cout * Cin * K * K = 8 * 3 * 25 float32 = 2400 bytes: out 2396 bytes past w overlaps it
+    (dict(out=FAKE + (1 << 30) + 2396), fc.FCONV_EINVAL, "overlaps"),
+])
+def test_conv2d_validation(kw, code, frag):
+    e = conv2d_err(**kw)
+    assert e.code == code
+    assert frag in e.message
+    assert "fconv2d_act_pool" in e.message
+
+
 def test_last_error_is_per_call():
     conv_err(N=0)
     assert ">= 1" in fc.fconv_last_error()

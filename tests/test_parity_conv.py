@@ -166,8 +166,8 @@ def test_conv_full_size_mish2_full_output_sampled():
 
 
 def test_conv_pool_repeated_calls_with_changing_shapes():
-    # The pooled path keeps per-image completion counters in the library's workspace;
-    # every call must leave them ready for the next one, whatever its shape.
+    # Calls share the library's cached workspace (repacked weights, pool partials), which
+    # grows on demand; every call must be right whatever shape the previous one had.
     cases = [(4, 16, 40, 36, 64), (2, 3, 17, 19, 8), (6, 20, 12, 70, 40), (4, 16, 40, 36, 64)]
     for k, shape in enumerate(cases * 2):
         bf16 = k % 3 == 1
