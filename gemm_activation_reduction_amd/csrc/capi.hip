@@ -33,59 +33,39 @@ constexpr long long kMaxElems = (1LL << 31) - 1;
 struct Workspace {
     void* ptr = nullptr;
     size_t bytes = 0;
-    unsigned* counters = nullptr;  // zero between calls: each kernel resets what it used
-    int ncounters = 0;
 };
 
 std::mutex g_ws_mutex;
 std::map<std::pair<int, hipStream_t>, Workspace> g_ws;
 
-// Returns device buffers owned by the library for (device, stream): a scratch area of at
-// least `bytes` and `ncounters` zero-initialized counter words. Growth waits for the
-// stream (earlier work may still use the old buffers) before freeing.
-int get_workspace(hipStream_t stream, size_t bytes, int ncounters, void** out, unsigned** counters) {
+// Returns a device buffer of at least `bytes` owned by the library for (current device,
+// stream). Growing it waits for the stream first (earlier work on it may still read the
+// old buffer) and then replaces the buffer; calls on other streams use their own.
+int get_workspace(hipStream_t stream, size_t bytes, void** out) {
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return fail(FCONV_EHIP, std::string("hipGetDevice: ") + hipGetErrorString(e));
     std::lock_guard<std::mutex> lock(g_ws_mutex);
     Workspace& ws = g_ws[std::make_pair(dev, stream)];
-    if (ws.bytes < bytes || ws.ncounters < ncounters) {
-        if (ws.ptr || ws.counters) {
+    if (ws.bytes < bytes) {
+        if (ws.ptr) {
             e = hipStreamSynchronize(stream);
             if (e != hipSuccess)
                 return fail(FCONV_EHIP, std::string("hipStreamSynchronize: ") + hipGetErrorString(e));
-        }
-        if (ws.bytes < bytes) {
             (void)hipFree(ws.ptr);
             ws.ptr = nullptr;
             ws.bytes = 0;
-            size_t want = bytes < (1u << 20) ? (1u << 20) : bytes;
-            e = hipMalloc(&ws.ptr, want);
-            if (e != hipSuccess) {
-                ws.ptr = nullptr;
-                (void)hipGetLastError();
-                return fail(FCONV_ENOMEM, "workspace hipMalloc(" + std::to_string(want) + "): " + hipGetErrorString(e));
-            }
-            ws.bytes = want;
         }
-        if (ws.ncounters < ncounters) {
-            (void)hipFree(ws.counters);
-            ws.counters = nullptr;
-            ws.ncounters = 0;
-            int want = ncounters < 4096 ? 4096 : ncounters;
-            e = hipMalloc(&ws.counters, (size_t)want * sizeof(unsigned));
-            if (e == hipSuccess) e = hipMemset(ws.counters, 0, (size_t)want * sizeof(unsigned));
-            if (e != hipSuccess) {
-                (void)hipFree(ws.counters);
-                ws.counters = nullptr;
-                (void)hipGetLastError();
-                return fail(FCONV_ENOMEM, std::string("workspace counters: ") + hipGetErrorString(e));
-            }
-            ws.ncounters = want;
+        const size_t want = bytes < (1u << 20) ? (1u << 20) : bytes;
+        e = hipMalloc(&ws.ptr, want);
+        if (e != hipSuccess) {
+            ws.ptr = nullptr;
+            (void)hipGetLastError();
+            return fail(FCONV_ENOMEM, "workspace hipMalloc(" + std::to_string(want) + "): " + hipGetErrorString(e));
         }
+        ws.bytes = want;
     }
     *out = ws.ptr;
-    if (counters) *counters = ws.counters;
     return FCONV_OK;
 }
 
@@ -209,7 +189,7 @@ int conv_impl(const char* name, const void* x, const void* w, const float* b, in
     if ((long long)Cin * H * W * (long long)esz > 0x7FFF0000LL || (long long)plan.wpack_bytes > 0x7FFF0000LL)
         return fail(FCONV_EUNSUPPORTED, fn + ": one image (or the weights) exceeds 2 GiB");
     void* ws = nullptr;
-    int rc = get_workspace(stream, plan.workspace_bytes(), 0, &ws, nullptr);
+    int rc = get_workspace(stream, plan.workspace_bytes(), &ws);
     if (rc != FCONV_OK) return rc;
     hipError_t e = fast ? fconv::launch_conv(plan, x, w, b, out, ws, stream, active_timer())
                         : fconv::launch_conv_general(plan, x, w, b, out, ws, stream, active_timer());
@@ -249,7 +229,7 @@ int gemm_lse_mish_impl(const char* name, bool bf16, const void* x, const void* w
     const fconv::GemmPlan plan = fconv::plan_gemm(bf16, M, K, N, x, w);
     if ((long long)plan.tilesM * plan.tilesN > 0x7FFFFFFFLL) return fail(FCONV_EUNSUPPORTED, fn + ": launch grid too large");
     void* ws = nullptr;
-    int rc = get_workspace(stream, plan.workspace_bytes(), 0, &ws, nullptr);
+    int rc = get_workspace(stream, plan.workspace_bytes(), &ws);
     if (rc != FCONV_OK) return rc;
     hipError_t e = fconv::launch_gemm_lse(plan, x, w, b, scale, cmin, cmax, out, ws, stream, active_timer());
     if (e != hipSuccess) return fail(FCONV_EHIP, fn + " launch: " + hipGetErrorString(e));
@@ -319,10 +299,10 @@ FCONV_API int fconv_release(void) {
     int cur = 0;
     const bool have_dev = hipGetDevice(&cur) == hipSuccess;
     for (auto& kv : g_ws) {
-        if (!kv.second.ptr && !kv.second.counters) continue;
+        if (!kv.second.ptr) continue;
         // A device-wide sync: the stream itself may already have been destroyed.
         if (hipSetDevice(kv.first.first) != hipSuccess || hipDeviceSynchronize() != hipSuccess ||
-            hipFree(kv.second.ptr) != hipSuccess || hipFree(kv.second.counters) != hipSuccess)
+            hipFree(kv.second.ptr) != hipSuccess)
             rc = fail(FCONV_EHIP, "fconv_release: HIP error while freeing a workspace");
     }
     g_ws.clear();
