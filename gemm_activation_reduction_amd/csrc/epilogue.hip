@@ -4,7 +4,8 @@
 //                     ("Kimi-K2.6 l2_p67": GELU + AdaptiveAvgPool2d(1) over the conv output);
 //   act_elementwise   act over a given tensor ("Kimi-K2.6 l2_p4": Mish applied twice);
 //   scale_clamp_lse   scale, clamp, row logsumexp and z * mish(z) over a given [M][N]
-//                     matrix ("Kimi-K2.6 l2_p22": the fused kernel after nn.Linear).
+//                     matrix ("Kimi-K2.6 l2_p22": the fused kernel after nn.Linear);
+//                     one read of each row when the clamp range bounds the exponentials.
 // Reductions are fixed-order (per-thread strided sums, wave64 butterflies, then waves
 // in order through LDS), so results are deterministic run to run.
 #include <cstdint>
@@ -80,36 +81,44 @@ __global__ __launch_bounds__(kThreads) void act_elementwise(const float* x, floa
     }
 }
 
-// One workgroup per row: c = clamp(scale * y); z = M + log(sum exp(c - M)), M = max c
-// (two passes; the second reads the row back from L2), then out = z * mish(z) with the
-// overflow-free softplus max(z,0) + log1p(e^-|z|).
-template <bool VEC>
+// One workgroup per row: c = clamp(scale * y), z = log(sum_j exp(c_j)), out = z * mish(z)
+// with the overflow-free softplus max(z,0) + log1p(e^-|z|). Logsumexp is invariant to the
+// shift it is evaluated around, so any shift at or above the row maximum is exact up to
+// rounding. ONE_PASS: every c lies in [cmin, cmax], so shifting by cmax bounds each term
+// in [e^(cmin - cmax), 1] -- no overflow, and with cmax - cmin <= 80 no term underflows in
+// fp32 -- and the row is read once. Otherwise the row maximum is found first and the
+// second pass reads the row again (from L2).
+template <bool VEC, bool ONE_PASS>
 __global__ __launch_bounds__(kThreads) void scale_clamp_lse(const float* __restrict__ y, float* __restrict__ out,
                                                            int N, float scale, float cmin, float cmax) {
     __shared__ float red[4];
     __shared__ float s_max;
     const float* r = y + (long long)blockIdx.x * N;
     auto clampv = [&](float v) { return fminf(fmaxf(scale * v, cmin), cmax); };
-    float m = -INFINITY;
-    if constexpr (VEC) {
-        for (int k = threadIdx.x; k < (N >> 2); k += kThreads) {
-            const f4 v = ((const f4*)r)[k];
-            m = fmaxf(m, fmaxf(fmaxf(clampv(v.x), clampv(v.y)), fmaxf(clampv(v.z), clampv(v.w))));
+    float mx = cmax;
+    if constexpr (!ONE_PASS) {
+        float m = -INFINITY;
+        if constexpr (VEC) {
+            for (int k = threadIdx.x; k < (N >> 2); k += kThreads) {
+                const f4 v = ((const f4*)r)[k];
+                m = fmaxf(m, fmaxf(fmaxf(clampv(v.x), clampv(v.y)), fmaxf(clampv(v.z), clampv(v.w))));
+            }
+        } else {
+            for (int k = threadIdx.x; k < N; k += kThreads) m = fmaxf(m, clampv(r[k]));
         }
-    } else {
-        for (int k = threadIdx.x; k < N; k += kThreads) m = fmaxf(m, clampv(r[k]));
+        m = wave_max(m);
+        const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+        if (lane == 0) red[wave] = m;
+        __syncthreads();
+        if (threadIdx.x == 0) s_max = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+        __syncthreads();
+        mx = s_max;
     }
-    m = wave_max(m);
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    if (lane == 0) red[wave] = m;
-    __syncthreads();
-    if (threadIdx.x == 0) s_max = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-    __syncthreads();
-    const float mx = s_max;
     float s = 0.0f;
     if constexpr (VEC) {
+#pragma unroll 4
         for (int k = threadIdx.x; k < (N >> 2); k += kThreads) {
-            const f4 v = ((const f4*)r)[k];
+            const f4 v = ONE_PASS ? __builtin_nontemporal_load((const f4*)r + k) : ((const f4*)r)[k];
             s += (fast_exp(clampv(v.x) - mx) + fast_exp(clampv(v.y) - mx)) +
                  (fast_exp(clampv(v.z) - mx) + fast_exp(clampv(v.w) - mx));
         }
@@ -178,12 +187,16 @@ hipError_t launch_act_elementwise(const float* x, long long count, int act, floa
 hipError_t launch_scale_clamp_lse(const float* y, int M, int N, float scale, float cmin, float cmax, float* out,
                                   hipStream_t stream) {
     const bool vec = N % 4 == 0 && (uintptr_t)y % 16 == 0;
-    if (vec)
-        hipLaunchKernelGGL((scale_clamp_lse<true>), dim3((unsigned)M), dim3(kThreads), 0, stream, y, out, N, scale,
-                           cmin, cmax);
+    const bool one = (double)cmax - (double)cmin <= 80.0;
+    const dim3 grid((unsigned)M), block(kThreads);
+    if (vec && one)
+        hipLaunchKernelGGL((scale_clamp_lse<true, true>), grid, block, 0, stream, y, out, N, scale, cmin, cmax);
+    else if (vec)
+        hipLaunchKernelGGL((scale_clamp_lse<true, false>), grid, block, 0, stream, y, out, N, scale, cmin, cmax);
+    else if (one)
+        hipLaunchKernelGGL((scale_clamp_lse<false, true>), grid, block, 0, stream, y, out, N, scale, cmin, cmax);
     else
-        hipLaunchKernelGGL((scale_clamp_lse<false>), dim3((unsigned)M), dim3(kThreads), 0, stream, y, out, N, scale,
-                           cmin, cmax);
+        hipLaunchKernelGGL((scale_clamp_lse<false, false>), grid, block, 0, stream, y, out, N, scale, cmin, cmax);
     return hipGetLastError();
 }
 

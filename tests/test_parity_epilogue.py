@@ -58,7 +58,10 @@ def test_act_elementwise_in_place_misaligned_and_empty():
 
 
 @pytest.mark.parametrize("M,N", [(1, 1), (3, 5), (37, 1000), (16, 8192), (5, 6147)])
-@pytest.mark.parametrize("scale,cmin,cmax", [(4.0, -10.0, 10.0), (-2.0, -0.5, 3.0)])
+# clamp ranges of at most 80 take the one-pass kernel (shift by cmax), wider ones the
+# two-pass max-shifted kernel: 80 exactly, just past it, and an unbounded clamp
+@pytest.mark.parametrize("scale,cmin,cmax", [(4.0, -10.0, 10.0), (-2.0, -0.5, 3.0), (30.0, -40.0, 40.0),
+                                             (30.0, -40.0, 40.5), (3.0, -1e30, 1e30)])
 def test_lse_mish_rows(M, N, scale, cmin, cmax):
     y = rand(M * 7 + N, (M, N))
     got = fc.lse_mish_rows(to_device(y), scale, cmin, cmax)
@@ -74,6 +77,11 @@ def test_lse_mish_rows_all_clamped():
     y = np.full((4, N), 7.0, np.float32)
     got = fc.lse_mish_rows(to_device(y), 4.0, -10.0, 10.0).cpu().numpy()[:, 0]
     z = 10.0 + math.log(N)
+    assert max_rel_err(got, np.full(4, z * z * math.tanh(math.log1p(math.exp(z))))) <= TOL_F32
+    # every value at the lower clamp, 80 below the shift: each term is e^-80, still normal in fp32
+    y = np.full((4, N), -7.0, np.float32)
+    got = fc.lse_mish_rows(to_device(y), 4.0, -40.0, 40.0).cpu().numpy()[:, 0]
+    z = -40.0 + math.log(N)
     assert max_rel_err(got, np.full(4, z * z * math.tanh(math.log1p(math.exp(z))))) <= TOL_F32
 
 
