@@ -42,12 +42,11 @@ constexpr int kThreads = 256;
 constexpr int kRow = 80;  // bytes per LDS row (64 data + 16 pad)
 
 
-template <int TH_, int TW_, int BN_, int WP_, int WO_, int MINW_, int PFD_, int NT_>
+template <int TH_, int TW_, int BN_, int WP_, int WO_, int MINW_, int NT_>
 struct Tile {
     static constexpr int TH = TH_, TW = TW_, BN = BN_, WP = WP_, WO = WO_;
     static constexpr int NT = NT_;              // threads per workgroup (NT / 64 waves)
     static constexpr int MINW = MINW_;          // waves per SIMD the register budget targets
-    static constexpr int PFD = PFD_;            // halo prefetch depth in K chunks (1 or 2)
     static constexpr int CB = TW / 16;          // 16-pixel blocks per tile row
     static constexpr int PB = TH * CB;          // pixel blocks per tile
     static constexpr int OB = BN / 16;          // oc blocks per tile
@@ -63,12 +62,12 @@ struct Tile {
     static_assert(TW % 16 == 0 && BN % 16 == 0, "MFMA block multiples");
 };
 
-// Tile configurations (index = ConvPlan::tile_cfg).
+// Tile configurations.
 // fp32: 256 pixels x 64 oc; wave = 4 pixel blocks x 4 oc blocks; 2 workgroups per CU.
-using TileA = Tile<8, 32, 64, 4, 1, 2, 1, 256>;
+using TileA = Tile<8, 32, 64, 4, 1, 2, 256>;
 // bf16: the same tile shape (measured on MI355X: a 256 x 128 tile with 8 waves and one
 // workgroup per CU, or 32-oc tiles with 3 workgroups per CU, were both slower).
-using TileB = Tile<8, 32, 64, 4, 1, 2, 1, 256>;
+using TileB = Tile<8, 32, 64, 4, 1, 2, 256>;
 
 
 // ---------------------------------------------------------------------------------
@@ -310,45 +309,20 @@ __global__ __launch_bounds__(TL::NT) __attribute__((amdgpu_waves_per_eu(TL::MINW
 
     using Halo = typename std::conditional<VEC, HaloVec<BF16, TL>, HaloScalar<BF16, TL>>::type;
     WeightStage<BF16, TL> wsg;
-    if constexpr (TL::PFD == 1) {
-        // One chunk ahead: the next chunk's loads fly while this chunk computes.
-        Halo hs;
-        hs.load(xr, H, W, Cin, 0, oh0, ow0, tid);
-        wsg.load(wr, CoutPad, 0, oc0, tid);
-        for (int ch = 0; ch < nChunk; ++ch) {
-            if (ch) __syncthreads();  // every wave is done reading the previous chunk
-            hs.store(halo, tid);
-            wsg.store(wl, tid);
-            __syncthreads();
-            if (ch + 1 < nChunk) {
-                hs.load(xr, H, W, Cin, (ch + 1) * CK, oh0, ow0, tid);
-                wsg.load(wr, CoutPad, ch + 1, oc0, tid);
-            }
-            compute_chunk();
+    // One chunk ahead: the next chunk's loads fly while this chunk computes.
+    Halo hs;
+    hs.load(xr, H, W, Cin, 0, oh0, ow0, tid);
+    wsg.load(wr, CoutPad, 0, oc0, tid);
+    for (int ch = 0; ch < nChunk; ++ch) {
+        if (ch) __syncthreads();  // every wave is done reading the previous chunk
+        hs.store(halo, tid);
+        wsg.store(wl, tid);
+        __syncthreads();
+        if (ch + 1 < nChunk) {
+            hs.load(xr, H, W, Cin, (ch + 1) * CK, oh0, ow0, tid);
+            wsg.load(wr, CoutPad, ch + 1, oc0, tid);
         }
-    } else {
-        // Halo tiles two chunks ahead (two register sets, alternating), weights one ahead.
-        Halo h0, h1;
-        h0.load(xr, H, W, Cin, 0, oh0, ow0, tid);
-        wsg.load(wr, CoutPad, 0, oc0, tid);
-        if (nChunk > 1) h1.load(xr, H, W, Cin, CK, oh0, ow0, tid);
-        for (int ch = 0; ch < nChunk; ch += 2) {
-            if (ch) __syncthreads();
-            h0.store(halo, tid);
-            wsg.store(wl, tid);
-            __syncthreads();
-            if (ch + 2 < nChunk) h0.load(xr, H, W, Cin, (ch + 2) * CK, oh0, ow0, tid);
-            if (ch + 1 < nChunk) wsg.load(wr, CoutPad, ch + 1, oc0, tid);
-            compute_chunk();
-            if (ch + 1 >= nChunk) break;
-            __syncthreads();
-            h1.store(halo, tid);
-            wsg.store(wl, tid);
-            __syncthreads();
-            if (ch + 3 < nChunk) h1.load(xr, H, W, Cin, (ch + 3) * CK, oh0, ow0, tid);
-            if (ch + 2 < nChunk) wsg.load(wr, CoutPad, ch + 2, oc0, tid);
-            compute_chunk();
-        }
+        compute_chunk();
     }
 
     // Epilogue. Accumulator layout (16x16 MFMA output): lane (g, i) register r holds
@@ -473,7 +447,6 @@ ConvPlan plan_conv(bool bf16, int act, int pool, int N, int Cin, int H, int W, i
     p.N = N; p.Cin = Cin; p.H = H; p.W = W; p.Cout = Cout;
     p.OH = H - 2; p.OW = W - 2;
     p.KS = 3; p.stride = 1; p.pad = 0; p.general = false;
-    p.tile_cfg = bf16 ? 1 : 0;
     p.TH = bf16 ? TileB::TH : TileA::TH;
     p.TW = bf16 ? TileB::TW : TileA::TW;
     p.BN = bf16 ? TileB::BN : TileA::BN;

@@ -21,7 +21,6 @@ struct ConvPlan {
     int OH, OW;
     int KS, stride, pad;     // kernel size, stride, zero padding (3, 1, 0 on the 3x3 valid path)
     bool general;            // planned for the general-geometry kernel
-    int tile_cfg;            // index of the tile configuration used
     int TH, TW, BN, CK;      // output tile rows/cols, oc per workgroup, channels per K chunk
     int tilesH, tilesW, ocTiles, nChunk, CoutPad;
     size_t wpack_bytes;      // repacked weights [nChunk][KS * KS][CoutPad][CK]
