@@ -175,3 +175,39 @@ def test_conv_pool_repeated_calls_with_changing_shapes():
         got = run_conv(x, w, b, fc.ACT_GELU, 1, bf16)
         ref = oracle.conv_act_pool(x, w, b, fc.ACT_GELU, 1)
         assert max_rel_err(got, ref) <= (TOL_BF16 if bf16 else TOL_F32), (k, shape)
+
+
+def test_conv_image_near_the_32bit_offset_limit():
+    # One image of x is 16 x 10000 x 3300 float32 = 2.112e9 bytes, just under the 2 GiB
+    # per-image bound the staging loads' 32-bit byte offsets allow (the library rejects
+    # larger images with FCONV_EUNSUPPORTED). The input repeats a seeded base of 2^24
+    # normals; outputs are checked at random points and along the last rows and columns,
+    # whose halo loads use the largest offsets.
+    N, Cin, H, W, Cout = 1, 16, 10000, 3300, 8
+    assert Cin * H * W * 4 < 0x7FFF0000
+    base = synth.normal(synth.seed_for(40, 0), 1 << 24)
+    x = np.resize(base, (N, Cin, H, W))
+    w = synth.uniform(synth.seed_for(40, 1), Cout * Cin * 9, -1 / 12, 1 / 12).reshape(Cout, Cin, 3, 3)
+    b = synth.uniform(synth.seed_for(40, 2), Cout, -0.1, 0.1)
+    xd = to_device(x)
+    del x
+    print("near-limit image: running GPU", flush=True)
+    out = fc.conv_act_pool(xd, to_device(w), to_device(b), act="gelu", pool=False)
+    torch.cuda.synchronize()
+    OH, OW = H - 2, W - 2
+    assert out.shape == (N, Cout, OH, OW) and bool(torch.isfinite(out).all())
+    r = np.random.default_rng(41)
+    cnt = 20000
+    oc, oh, ow = r.integers(0, Cout, cnt), r.integers(0, OH, cnt), r.integers(0, OW, cnt)
+    edge_c = np.arange(OW)
+    oc = np.concatenate([oc, np.full(OW, Cout - 1), np.full(OH, Cout - 1)])
+    oh = np.concatenate([oh, np.full(OW, OH - 1), np.arange(OH)])
+    ow = np.concatenate([ow, edge_c, np.full(OH, OW - 1)])
+    n = np.zeros_like(oc)
+    idx = [torch.from_numpy(a.astype(np.int64)).cuda() for a in (n, oc, oh, ow)]
+    got = out[idx[0], idx[1], idx[2], idx[3]].cpu().numpy()
+    del out, xd
+    ref = oracle.conv_point_sample(np.resize(base, (N, Cin, H, W)), w, b, fc.ACT_GELU, n, oc, oh, ow)
+    err = max_rel_err(got, ref)
+    print(f"near-limit image: sampled err={err:.3e}", flush=True)
+    assert err <= TOL_F32
