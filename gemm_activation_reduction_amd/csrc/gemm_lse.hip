@@ -58,6 +58,9 @@ struct GTile {
 // 256 x 192 tiles: 2048 x 6144 is exactly 256 tiles, one per CU; 8 waves of 64 x 96.
 using GTileF = GTile<256, 192, 4, 2, 32, 512, false>;
 using GTileH = GTile<256, 192, 4, 2, 64, 512, true>;
+// bf16 on the LDS-DMA path: the same tile with 64-byte K stages, four stages in flight.
+using GTileD = GTile<256, 192, 4, 2, 32, 512, true>;
+constexpr int kDmaStages = 4;
 
 // One 16-byte group of K elements of one row (PER16 elements from k on); out-of-range
 // rows and elements read as zero.
@@ -86,6 +89,70 @@ __device__ __forceinline__ f4 load16(const typename GElem<BF16>::T* __restrict__
             d[e] = lo | (hi << 16);
         }
         return __builtin_bit_cast(f4, d);
+    }
+}
+
+// Tile epilogue shared by both GEMM kernels. Lane (g, i) register r of acc[jm][jn] holds
+// row rm0 + 16 jm + 4g + r, column rn0 + 16 jn + i of the tile. Applies bias, scale and
+// clamp, reduces each row to (max, sum exp(c - max)) (16-lane butterflies, then the WN
+// column slices through `red`, LDS the caller no longer needs) and writes part[m][tn].
+template <class TL>
+__device__ __forceinline__ void tile_epilogue(f4 (&acc)[TL::MB][TL::NB], float2* red, const float* __restrict__ bias,
+                                              float2* __restrict__ part, int m0, int n0, int M, int N, int tn,
+                                              int tilesN, float scale, float cmin, float cmax, int tid, int g, int i,
+                                              int wn, int rm0, int rn0) {
+    // Epilogue: lane (g, i) register r holds row rm0 + 16 jm + 4g + r, column rn0 + 16 jn + i.
+    float bv[TL::NB];
+    bool cv[TL::NB];
+#pragma unroll
+    for (int jn = 0; jn < TL::NB; ++jn) {
+        const int n = n0 + rn0 + jn * 16 + i;
+        cv[jn] = n < N;
+        bv[jn] = cv[jn] ? bias[n] : 0.0f;
+    }
+    float rmax[TL::MB][4], rsum[TL::MB][4];
+#pragma unroll
+    for (int jm = 0; jm < TL::MB; ++jm) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            float mx = -INFINITY;
+#pragma unroll
+            for (int jn = 0; jn < TL::NB; ++jn) {
+                const float c = fminf(fmaxf(scale * (acc[jm][jn][r] + bv[jn]), cmin), cmax);
+                acc[jm][jn][r] = c;
+                mx = cv[jn] ? fmaxf(mx, c) : mx;
+            }
+#pragma unroll
+            for (int off = 8; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 64));
+            float s = 0.0f;
+#pragma unroll
+            for (int jn = 0; jn < TL::NB; ++jn) s += cv[jn] ? fast_exp(acc[jm][jn][r] - mx) : 0.0f;
+#pragma unroll
+            for (int off = 8; off >= 1; off >>= 1) s += __shfl_xor(s, off, 64);
+            rmax[jm][r] = mx;
+            rsum[jm][r] = s;
+        }
+    }
+    // Merge the WN column slices of each row through LDS (the caller ended on a barrier).
+    if (i == 0) {
+#pragma unroll
+        for (int jm = 0; jm < TL::MB; ++jm)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                red[wn * TL::BM + rm0 + jm * 16 + 4 * g + r] = make_float2(rmax[jm][r], rsum[jm][r]);
+    }
+    __syncthreads();
+    if (tid < TL::BM && m0 + tid < M) {
+        float mx = -INFINITY;
+#pragma unroll
+        for (int w = 0; w < TL::WN; ++w) mx = fmaxf(mx, red[w * TL::BM + tid].x);
+        float s = 0.0f;
+#pragma unroll
+        for (int w = 0; w < TL::WN; ++w) {
+            const float2 p = red[w * TL::BM + tid];
+            s += p.y > 0.0f ? p.y * fast_exp(p.x - mx) : 0.0f;
+        }
+        part[(long long)(m0 + tid) * tilesN + tn] = make_float2(mx, s);
     }
 }
 
@@ -183,60 +250,136 @@ __global__ __launch_bounds__(TL::NT) void gemm_lse_partials(
         __syncthreads();
     }
 
-    // Epilogue: lane (g, i) register r holds row rm0 + 16 jm + 4g + r, column rn0 + 16 jn + i.
-    float bv[TL::NB];
-    bool cv[TL::NB];
+    tile_epilogue<TL>(acc, (float2*)&As[0][0], bias, part, m0, n0, M, N, tn, tilesN, scale, cmin, cmax, tid, g, i,
+                      wn, rm0, rn0);
+}
+
+// bf16 operands on the LDS-DMA path: each K stage is 32 values (64 bytes) of every tile
+// row, loaded by buffer_load_dwordx4 ... lds straight into one of STAGES LDS buffers,
+// STAGES-1 stages ahead of the MFMA work (no registers, no LDS store instructions). A
+// wave's DMA instruction fills 1 KB of LDS in lane order: 16 rows x 4 slots. Rows carry
+// no padding; instead slot s of a row whose index within its 16-row block is r holds
+// K group s ^ f(r), f(r) = ((r >> 1) ^ (r >> 3)) & 3, which keeps the fragment reads
+// (16 rows x 4 groups per wave) on distinct banks. Out-of-range rows and K groups read
+// zero through the buffer resource. Taken for K % 64 == 0 (whole 16-byte groups and an
+// even number of stages) and operands under 2 GiB.
+template <class TL, int STAGES>
+__global__ __launch_bounds__(TL::NT) void gemm_lse_partials_dma(
+    const unsigned short* __restrict__ X, const unsigned short* __restrict__ Wt, const float* __restrict__ bias,
+    float2* __restrict__ part, int M, int K, int N, float scale, float cmin, float cmax, int tilesN) {
+    static_assert(TL::BF16 && TL::KG == 4, "64-byte bf16 K stages");
+    constexpr int BK = TL::BK, ROWS = TL::BM + TL::BN, SB = ROWS * 64;  // bytes per stage
+    constexpr int NI = ROWS / 16, NW = TL::NT / 64;                       // DMA instructions per stage, waves
+    static_assert(ROWS % 16 == 0 && TL::BM % 16 == 0, "whole 16-row DMA blocks");
+    __shared__ __attribute__((aligned(1024))) unsigned char lds[STAGES * SB];
+
+    const int tn = blockIdx.x % tilesN, tm = blockIdx.x / tilesN;
+    const int m0 = tm * TL::BM, n0 = tn * TL::BN;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int g = lane >> 4, i = lane & 15;
+    const int wm = wave % TL::WM, wn = wave / TL::WM;
+    const int rm0 = wm * TL::MB * 16, rn0 = wn * TL::NB * 16;
+
+    f4 acc[TL::MB][TL::NB];
 #pragma unroll
-    for (int jn = 0; jn < TL::NB; ++jn) {
-        const int n = n0 + rn0 + jn * 16 + i;
-        cv[jn] = n < N;
-        bv[jn] = cv[jn] ? bias[n] : 0.0f;
-    }
-    float rmax[TL::MB][4], rsum[TL::MB][4];
+    for (int a = 0; a < TL::MB; ++a)
 #pragma unroll
-    for (int jm = 0; jm < TL::MB; ++jm) {
+        for (int b = 0; b < TL::NB; ++b) acc[a][b] = f4{0.f, 0.f, 0.f, 0.f};
+
+    const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc((void*)X, (short)0, M * K * 2, 0x00020000);
+    const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc((void*)Wt, (short)0, N * K * 2, 0x00020000);
+    constexpr int kOOB = 0x7FFFFFF0;
+    // DMA lane -> (row within the 16-row block, K group): physical slot lane & 3 holds
+    // group (lane & 3) ^ f(lane >> 2).
+    const int dma_r = lane >> 2;
+    const int dma_grp = (lane & 3) ^ (((dma_r >> 1) ^ (dma_r >> 3)) & 3);
+    auto issue = [&](int buf, int k0) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            float mx = -INFINITY;
-#pragma unroll
-            for (int jn = 0; jn < TL::NB; ++jn) {
-                const float c = fminf(fmaxf(scale * (acc[jm][jn][r] + bv[jn]), cmin), cmax);
-                acc[jm][jn][r] = c;
-                mx = cv[jn] ? fmaxf(mx, c) : mx;
+        for (int q = 0; q < (NI + NW - 1) / NW; ++q) {
+            const int ins = wave + NW * q;  // wave-uniform
+            if (ins < NI) {
+                const int row = ins * 16 + dma_r;
+                const int k = k0 + 8 * dma_grp;
+                typedef __attribute__((address_space(3))) void lds_t;
+                lds_t* dst = (lds_t*)(lds + buf * SB + ins * 1024);
+                if (ins * 16 < TL::BM) {
+                    const int r = m0 + row;
+                    const int off = (r < M && k < K) ? (r * K + k) * 2 : kOOB;
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, dst, 16, off, 0, 0, 0);
+                } else {
+                    const int r = n0 + row - TL::BM;
+                    const int off = (r < N && k < K) ? (r * K + k) * 2 : kOOB;
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, dst, 16, off, 0, 0, 0);
+                }
             }
-#pragma unroll
-            for (int off = 8; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 64));
-            float s = 0.0f;
-#pragma unroll
-            for (int jn = 0; jn < TL::NB; ++jn) s += cv[jn] ? fast_exp(acc[jm][jn][r] - mx) : 0.0f;
-#pragma unroll
-            for (int off = 8; off >= 1; off >>= 1) s += __shfl_xor(s, off, 64);
-            rmax[jm][r] = mx;
-            rsum[jm][r] = s;
         }
+    };
+    // this wave's DMA instructions per stage
+    const int per_stage = (NI - wave + NW - 1) / NW;
+    // fragment read offset of lane (g, i): group g of row i sits in slot g ^ f(i)
+    const int frag_off = i * 64 + 16 * (g ^ (((i >> 1) ^ (i >> 3)) & 3));
+
+    // Waits until this wave's DMA of stage `st` has landed, allowing its DMA of the stages
+    // issued after it (up to `last`) to stay in flight, then a bare barrier (not
+    // __syncthreads, whose release fence would wait for every DMA in flight): afterwards
+    // stage st is in LDS for every wave, and every wave's earlier LDS reads are done.
+    // s_waitcnt immediates (gfx9 encoding: vmcnt bits [3:0] and [15:14], expcnt [6:4],
+    // lgkmcnt [11:8]): vmcnt(n) and lgkmcnt(0) together, expcnt not waited on. Issued
+    // through the builtin so the compiler's own wait insertion knows the counters drained.
+    auto stage_ready = [&](int st, int last) {
+        const int inflight = (last > st ? last - st : 0) * per_stage;
+        __asm__ volatile("" ::: "memory");  // the LDS reads issued above stay above the wait
+        if (inflight >= 8) __builtin_amdgcn_s_waitcnt(0x0078);
+        else if (inflight >= 6) __builtin_amdgcn_s_waitcnt(0x0076);
+        else if (inflight >= 4) __builtin_amdgcn_s_waitcnt(0x0074);
+        else if (inflight >= 3) __builtin_amdgcn_s_waitcnt(0x0073);
+        else __builtin_amdgcn_s_waitcnt(0x0070);
+        __builtin_amdgcn_s_barrier();
+        __asm__ volatile("" ::: "memory");
+    };
+    // lane (g, i) fragment of stage st for 16-row block j of the A rows / B rows
+    auto frag_a = [&](int st, int j) { return *(const f4*)(lds + (st % STAGES) * SB + (rm0 + j * 16) * 64 + frag_off); };
+    auto frag_b = [&](int st, int j) {
+        return *(const f4*)(lds + (st % STAGES) * SB + (TL::BM + rn0 + j * 16) * 64 + frag_off);
+    };
+
+    // Pipeline. Step kt: read stage kt+1's fragments (into the other register set), the
+    // MFMA work of stage kt, the DMA of stage kt+STAGES-1 into the buffer stage kt-1 used,
+    // then wait for stage kt+2 and the barrier. The LDS reads of the next stage overlap
+    // this stage's MFMA work.
+    const int nk = (K + BK - 1) / BK;
+    const int lastIssued0 = (nk < STAGES - 1 ? nk : STAGES - 1) - 1;
+#pragma unroll
+    for (int st = 0; st < STAGES - 1; ++st)
+        if (st < nk) issue(st, st * BK);
+    f4 a0[TL::MB], b0[TL::NB], a1[TL::MB], b1[TL::NB];
+    stage_ready(0, lastIssued0);
+#pragma unroll
+    for (int j = 0; j < TL::MB; ++j) a0[j] = frag_a(0, j);
+#pragma unroll
+    for (int j = 0; j < TL::NB; ++j) b0[j] = frag_b(0, j);
+    stage_ready(1, lastIssued0);
+#define FCONV_DMA_STEP(KT, AC, BC, AN, BN_)                                                                      \
+    {                                                                                                            \
+        const int kt_ = (KT);                                                                                    \
+        /* the last step reads a stale ring slot it never uses: no branch around the reads */                    \
+        _Pragma("unroll") for (int j = 0; j < TL::MB; ++j) AN[j] = frag_a(kt_ + 1, j);                           \
+        _Pragma("unroll") for (int j = 0; j < TL::NB; ++j) BN_[j] = frag_b(kt_ + 1, j);                          \
+        _Pragma("unroll") for (int jm = 0; jm < TL::MB; ++jm)                                                    \
+            _Pragma("unroll") for (int jn = 0; jn < TL::NB; ++jn)                                                \
+                acc[jm][jn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(                                           \
+                    __builtin_bit_cast(bf16x8, AC[jm]), __builtin_bit_cast(bf16x8, BC[jn]), acc[jm][jn], 0, 0, 0); \
+        if (kt_ + STAGES - 1 < nk) issue((kt_ + STAGES - 1) % STAGES, (kt_ + STAGES - 1) * BK);                  \
+        stage_ready(kt_ + 2, nk - 1 < kt_ + STAGES - 1 ? nk - 1 : kt_ + STAGES - 1);                            \
     }
-    // Merge the WN column slices of each row through LDS (the main loop ended on a barrier).
-    float2* red = (float2*)&As[0][0];
-    if (i == 0) {
-#pragma unroll
-        for (int jm = 0; jm < TL::MB; ++jm)
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-                red[wn * TL::BM + rm0 + jm * 16 + 4 * g + r] = make_float2(rmax[jm][r], rsum[jm][r]);
+    for (int kt = 0; kt < nk; kt += 2) {  // nk is even (K % 64 == 0 on this path)
+        FCONV_DMA_STEP(kt, a0, b0, a1, b1)
+        FCONV_DMA_STEP(kt + 1, a1, b1, a0, b0)
     }
-    __syncthreads();
-    if (tid < TL::BM && m0 + tid < M) {
-        float mx = -INFINITY;
-#pragma unroll
-        for (int w = 0; w < TL::WN; ++w) mx = fmaxf(mx, red[w * TL::BM + tid].x);
-        float s = 0.0f;
-#pragma unroll
-        for (int w = 0; w < TL::WN; ++w) {
-            const float2 p = red[w * TL::BM + tid];
-            s += p.y > 0.0f ? p.y * fast_exp(p.x - mx) : 0.0f;
-        }
-        part[(long long)(m0 + tid) * tilesN + tn] = make_float2(mx, s);
-    }
+#undef FCONV_DMA_STEP
+    __syncthreads();  // every wave is done with the stage buffers (the epilogue reuses them)
+    tile_epilogue<TL>(acc, (float2*)lds, bias, part, m0, n0, M, N, tn, tilesN, scale, cmin, cmax, tid, g, i, wn, rm0,
+                      rn0);
 }
 
 // One wave per row: fixed-order online-logsumexp merge of the tile partials, then
@@ -288,6 +431,10 @@ GemmPlan plan_gemm(bool bf16, int M, int K, int N, const void* x, const void* w)
     p.tilesM = (M + p.BM - 1) / p.BM;
     p.tilesN = (N + p.BN - 1) / p.BN;
     p.vec = (K % (bf16 ? 8 : 4) == 0) && (((size_t)x | (size_t)w) % 16 == 0);
+    // LDS-DMA path: bf16, whole 16-byte K groups, each operand addressable with 31-bit
+    // byte offsets (the buffer resource's out-of-range offset must lie past its end).
+    p.dma = bf16 && p.vec && K % 64 == 0 && (long long)M * K * 2 < 0x7FFF0000LL &&
+            (long long)N * K * 2 < 0x7FFF0000LL;
     p.part_bytes = (size_t)M * p.tilesN * sizeof(float2);
     return p;
 }
@@ -297,8 +444,16 @@ hipError_t launch_gemm_lse(const GemmPlan& p, const void* x, const void* w, cons
                            KernelTimer* timer) {
     float2* part = (float2*)workspace;
     if (timer) timer->begin("gemm_lse_partials", stream);
-    hipError_t e = p.bf16 ? launch_partials<GTileH>(p, x, w, b, scale, cmin, cmax, part, stream)
-                          : launch_partials<GTileF>(p, x, w, b, scale, cmin, cmax, part, stream);
+    hipError_t e;
+    if (p.dma) {
+        hipLaunchKernelGGL((gemm_lse_partials_dma<GTileD, kDmaStages>), dim3((unsigned)(p.tilesM * p.tilesN)),
+                           dim3(GTileD::NT), 0, stream, (const unsigned short*)x, (const unsigned short*)w, b, part,
+                           p.M, p.K, p.N, scale, cmin, cmax, p.tilesN);
+        e = hipGetLastError();
+    } else {
+        e = p.bf16 ? launch_partials<GTileH>(p, x, w, b, scale, cmin, cmax, part, stream)
+                   : launch_partials<GTileF>(p, x, w, b, scale, cmin, cmax, part, stream);
+    }
     if (timer) timer->end("gemm_lse_partials", stream);
     if (e != hipSuccess) return e;
     if (timer) timer->begin("lse_merge_mish", stream);

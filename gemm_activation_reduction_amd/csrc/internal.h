@@ -46,6 +46,7 @@ struct GemmPlan {
     int BM, BN;
     int tilesM, tilesN;
     bool vec;                // K a multiple of a 16-byte group, 16-byte aligned rows: dwordx4 loads
+    bool dma;                // bf16 LDS-DMA kernel (vec, operands under 2 GiB)
     size_t part_bytes;       // [M][tilesN] (max, sum) pairs
     size_t workspace_bytes() const { return part_bytes; }
 };
