@@ -322,7 +322,12 @@ __global__ __launch_bounds__(TL::NT) __attribute__((amdgpu_waves_per_eu(TL::MINW
             hs.load(xr, H, W, Cin, (ch + 1) * CK, oh0, ow0, tid);
             wsg.load(wr, CoutPad, ch + 1, oc0, tid);
         }
+        // bf16: while computing, this wave issues ahead of the co-resident workgroup's
+        // staging and epilogue VALU work on the same SIMD (measured +2 %; fp32, whose
+        // MFMAs are 8x longer, loses 2-3 % with it)
+        if constexpr (BF16) __builtin_amdgcn_s_setprio(1);
         compute_chunk();
+        if constexpr (BF16) __builtin_amdgcn_s_setprio(0);
     }
 
     // Epilogue. Accumulator layout (16x16 MFMA output): lane (g, i) register r holds
