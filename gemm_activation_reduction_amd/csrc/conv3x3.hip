@@ -5,10 +5,11 @@
 // shifted "tap GEMMs" over a halo tile held in LDS, on MFMA:
 //   fp32:  v_mfma_f32_16x16x4_f32   (full fp32 products, fp32 accumulation)
 //   bf16:  v_mfma_f32_16x16x32_bf16 (exact bf16 products, fp32 accumulation)
-// The activation runs on the accumulators in registers; with pooling, each
-// workgroup reduces its pixels per output channel (wave64 butterfly, then LDS
-// across waves) and writes one partial per (n, oc, tile); a second kernel sums
-// the partials in a fixed order, so the result is deterministic without atomics.
+// The accumulators start at the bias and the activation runs on them in registers;
+// with pooling, each workgroup reduces its pixels per output channel (wave64
+// butterfly, then LDS across waves) and writes one partial per (n, oc, tile); a
+// second kernel sums the partials in a fixed order, so the result is deterministic
+// without atomics.
 //
 // The operation is the Conv2d -> activation (-> AdaptiveAvgPool2d(1)) chain of
 // the "Kimi-K2.6 l2_p67" and "Kimi-K2.6 l2_p4" POPCORNBENCH pages; the pages'
@@ -259,11 +260,17 @@ __global__ __launch_bounds__(TL::NT) __attribute__((amdgpu_waves_per_eu(TL::MINW
     auto pb_row = [](int pb) { return BF16 ? pb / TL::CB : pb % TL::TH; };
     auto pb_col = [](int pb) { return BF16 ? pb % TL::CB : pb / TL::TH; };
 
+    // The accumulators start at the bias: lane (g, i) holds output channel i of each oc
+    // block in all four of its accumulator registers, so one value per oc block does, and
+    // the epilogue saves an add per output (VALU work here is not hidden under the MFMAs).
     f4 acc[TL::WPB][TL::WOB];
 #pragma unroll
-    for (int a = 0; a < TL::WPB; ++a)
+    for (int c = 0; c < TL::WOB; ++c) {
+        const int oc = oc0 + (woi * TL::WOB + c) * 16 + i;
+        const float bv = oc < Cout ? bias[oc] : 0.0f;
 #pragma unroll
-        for (int c = 0; c < TL::WOB; ++c) acc[a][c] = f4{0.f, 0.f, 0.f, 0.f};
+        for (int a = 0; a < TL::WPB; ++a) acc[a][c] = f4{bv, bv, bv, bv};
+    }
 
     const long long plane = (long long)H * W;
     const __amdgpu_buffer_rsrc_t xr = make_rsrc(x + (long long)n * Cin * plane, (unsigned)(Cin * plane * sizeof(T)));
@@ -333,29 +340,31 @@ __global__ __launch_bounds__(TL::NT) __attribute__((amdgpu_waves_per_eu(TL::MINW
     // Epilogue. Accumulator layout (16x16 MFMA output): lane (g, i) register r holds
     // pixel 4g + r of the pixel block and output channel i of the oc block.
     const bool interior = oh0 + TL::TH <= OH && ow0 + TL::TW <= OW;  // uniform per workgroup
-    float bv[TL::WOB];
-#pragma unroll
-    for (int j = 0; j < TL::WOB; ++j) {
-        const int oc = oc0 + (woi * TL::WOB + j) * 16 + i;
-        bv[j] = oc < Cout ? bias[oc] : 0.0f;
-    }
-
     if constexpr (POOL) {
         float psum[TL::WOB];
 #pragma unroll
         for (int j = 0; j < TL::WOB; ++j) psum[j] = 0.0f;
+        if (interior) {  // every pixel of the tile is an output: no masking
 #pragma unroll
-        for (int jp = 0; jp < TL::WPB; ++jp) {
-            const int pb = wpi * TL::WPB + jp;
-            const int oh = oh0 + pb_row(pb);
-            const int owb = ow0 + pb_col(pb) * 16 + 4 * g;
+            for (int jp = 0; jp < TL::WPB; ++jp)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const bool valid = interior || (oh < OH && owb + r < OW);
+                for (int r = 0; r < 4; ++r)
 #pragma unroll
-                for (int jo = 0; jo < TL::WOB; ++jo) {
-                    const float v = activate<ACT>(acc[jp][jo][r] + bv[jo]);
-                    psum[jo] += valid ? v : 0.0f;
+                    for (int jo = 0; jo < TL::WOB; ++jo) psum[jo] += activate<ACT>(acc[jp][jo][r]);
+        } else {
+#pragma unroll
+            for (int jp = 0; jp < TL::WPB; ++jp) {
+                const int pb = wpi * TL::WPB + jp;
+                const int oh = oh0 + pb_row(pb);
+                const int owb = ow0 + pb_col(pb) * 16 + 4 * g;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const bool valid = oh < OH && owb + r < OW;
+#pragma unroll
+                    for (int jo = 0; jo < TL::WOB; ++jo) {
+                        const float v = activate<ACT>(acc[jp][jo][r]);
+                        psum[jo] += valid ? v : 0.0f;
+                    }
                 }
             }
         }
@@ -393,7 +402,7 @@ __global__ __launch_bounds__(TL::NT) __attribute__((amdgpu_waves_per_eu(TL::MINW
                 if (oc >= Cout) continue;
                 float v[4];
 #pragma unroll
-                for (int r = 0; r < 4; ++r) v[r] = activate<ACT>(acc[jp][jo][r] + bv[jo]);
+                for (int r = 0; r < 4; ++r) v[r] = activate<ACT>(acc[jp][jo][r]);
                 float* o = dst + (((long long)n * Cout + oc) * OH + oh) * OW + owb;
                 // out_align: 16 / 8 / 4 = byte alignment of the output base pointer
                 if ((OW & 3) == 0 && out_align >= 16 && owb + 3 < OW) {
