@@ -58,8 +58,10 @@ struct GTile {
 // 256 x 192 tiles: 2048 x 6144 is exactly 256 tiles, one per CU; 8 waves of 64 x 96.
 using GTileF = GTile<256, 192, 4, 2, 32, 512, false>;
 using GTileH = GTile<256, 192, 4, 2, 64, 512, true>;
-// bf16 on the LDS-DMA path: the same tile with 64-byte K stages, four stages in flight.
+// LDS-DMA path: the same tile with 64-byte K stages (32 bf16 / 16 fp32 values), four
+// stages in flight.
 using GTileD = GTile<256, 192, 4, 2, 32, 512, true>;
+using GTileDF = GTile<256, 192, 4, 2, 16, 512, false>;
 constexpr int kDmaStages = 4;
 
 // One 16-byte group of K elements of one row (PER16 elements from k on); out-of-range
@@ -254,15 +256,21 @@ __global__ __launch_bounds__(TL::NT) void gemm_lse_partials(
                       wn, rm0, rn0);
 }
 
-// bf16 operands on the LDS-DMA path: each K stage is 32 values (64 bytes) of every tile
-// row, loaded by buffer_load_dwordx4 ... lds straight into one of STAGES LDS buffers,
+// LDS-DMA path (bf16 or fp32 operands): each K stage is 64 bytes (32 bf16 or 16 fp32
+// values) of every tile row, loaded by buffer_load_dwordx4 ... lds straight into one of
+// STAGES LDS buffers,
 // STAGES-1 stages ahead of the MFMA work (no registers, no LDS store instructions). A
 // wave's DMA instruction fills 1 KB of LDS in lane order: 16 rows x 4 slots. Rows carry
 // no padding; instead slot s of a row whose index within its 16-row block is r holds
 // K group s ^ f(r), f(r) = ((r >> 1) ^ (r >> 3)) & 3, which keeps the fragment reads
 // (16 rows x 4 groups per wave) on distinct banks. Out-of-range rows and K groups read
-// zero through the buffer resource. Taken for K % 64 == 0 (whole 16-byte groups and an
-// even number of stages) and operands under 2 GiB.
+// zero through the buffer resource. Taken when K is a whole even number of stages
+// (bf16: K % 64 == 0, fp32: K % 32 == 0) and operands are under 2 GiB. A lane's
+// 16-byte group feeds one bf16 16x16x32 MFMA or, element by element, four fp32
+// 16x16x4 MFMAs (the reduction order within the stage is free).
+// On gfx950 the VALU work of staging through registers (global loads, LDS stores,
+// address arithmetic) does not overlap fp32 MFMA work, so the DMA path pays off for
+// fp32 as well.
 // Instruction order of one DMA step (READS fragment reads of the next stage, MFMAS of this
 // one): two MFMAs, then one read, until the reads are issued, then the remaining MFMAs, so
 // the reads go out early and their latency hides under the MFMA work (measured: 1-2 %
@@ -281,9 +289,11 @@ __device__ __forceinline__ void dma_step_schedule() {
 
 template <class TL, int STAGES>
 __global__ __launch_bounds__(TL::NT) void gemm_lse_partials_dma(
-    const unsigned short* __restrict__ X, const unsigned short* __restrict__ Wt, const float* __restrict__ bias,
-    float2* __restrict__ part, int M, int K, int N, float scale, float cmin, float cmax, int tilesN) {
-    static_assert(TL::BF16 && TL::KG == 4, "64-byte bf16 K stages");
+    const typename GElem<TL::BF16>::T* __restrict__ X, const typename GElem<TL::BF16>::T* __restrict__ Wt,
+    const float* __restrict__ bias, float2* __restrict__ part, int M, int K, int N, float scale, float cmin,
+    float cmax, int tilesN) {
+    static_assert(TL::KG == 4, "64-byte K stages");
+    constexpr int ESZ = (int)sizeof(typename GElem<TL::BF16>::T), EPG = 16 / ESZ;  // bytes, values per group
     constexpr int BK = TL::BK, ROWS = TL::BM + TL::BN, SB = ROWS * 64;  // bytes per stage
     constexpr int NI = ROWS / 16, NW = TL::NT / 64;                       // DMA instructions per stage, waves
     static_assert(ROWS % 16 == 0 && TL::BM % 16 == 0, "whole 16-row DMA blocks");
@@ -306,8 +316,8 @@ __global__ __launch_bounds__(TL::NT) void gemm_lse_partials_dma(
 #pragma unroll
         for (int b = 0; b < TL::NB; ++b) acc[a][b] = f4{0.f, 0.f, 0.f, 0.f};
 
-    const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc((void*)X, (short)0, M * K * 2, 0x00020000);
-    const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc((void*)Wt, (short)0, N * K * 2, 0x00020000);
+    const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc((void*)X, (short)0, M * K * ESZ, 0x00020000);
+    const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc((void*)Wt, (short)0, N * K * ESZ, 0x00020000);
     constexpr int kOOB = 0x7FFFFFF0;
     // DMA lane -> (row within the 16-row block, K group): physical slot lane & 3 holds
     // group (lane & 3) ^ f(lane >> 2).
@@ -319,16 +329,16 @@ __global__ __launch_bounds__(TL::NT) void gemm_lse_partials_dma(
             const int ins = wave + NW * q;  // wave-uniform
             if (ins < NI) {
                 const int row = ins * 16 + dma_r;
-                const int k = k0 + 8 * dma_grp;
+                const int k = k0 + EPG * dma_grp;
                 typedef __attribute__((address_space(3))) void lds_t;
                 lds_t* dst = (lds_t*)(lds + buf * SB + ins * 1024);
                 if (ins * 16 < TL::BM) {
                     const int r = m0 + row;
-                    const int off = (r < M && k < K) ? (r * K + k) * 2 : kOOB;
+                    const int off = (r < M && k < K) ? (r * K + k) * ESZ : kOOB;
                     __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, dst, 16, off, 0, 0, 0);
                 } else {
                     const int r = n0 + row - TL::BM;
-                    const int off = (r < N && k < K) ? (r * K + k) * 2 : kOOB;
+                    const int off = (r < N && k < K) ? (r * K + k) * ESZ : kOOB;
                     __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, dst, 16, off, 0, 0, 0);
                 }
             }
@@ -390,11 +400,19 @@ __global__ __launch_bounds__(TL::NT) void gemm_lse_partials_dma(
         /* the last step reads a stale ring slot it never uses: no branch around the reads */                    \
         _Pragma("unroll") for (int j = 0; j < TL::MB; ++j) AN[j] = frag_a(kt_ + 1, j);                           \
         _Pragma("unroll") for (int j = 0; j < TL::NB; ++j) BN_[j] = frag_b(kt_ + 1, j);                          \
-        _Pragma("unroll") for (int jm = 0; jm < TL::MB; ++jm)                                                    \
-            _Pragma("unroll") for (int jn = 0; jn < TL::NB; ++jn)                                                \
-                acc[jm][jn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(                                           \
-                    __builtin_bit_cast(bf16x8, AC[jm]), __builtin_bit_cast(bf16x8, BC[jn]), acc[jm][jn], 0, 0, 0); \
-        dma_step_schedule<TL::MB + TL::NB, TL::MB * TL::NB>();                                                   \
+        if constexpr (TL::BF16) {                                                                                \
+            _Pragma("unroll") for (int jm = 0; jm < TL::MB; ++jm)                                                \
+                _Pragma("unroll") for (int jn = 0; jn < TL::NB; ++jn)                                            \
+                    acc[jm][jn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, AC[jm]),     \
+                        __builtin_bit_cast(bf16x8, BC[jn]), acc[jm][jn], 0, 0, 0);                                \
+        } else {                                                                                                 \
+            _Pragma("unroll") for (int s_ = 0; s_ < 4; ++s_)                                                     \
+                _Pragma("unroll") for (int jm = 0; jm < TL::MB; ++jm)                                            \
+                    _Pragma("unroll") for (int jn = 0; jn < TL::NB; ++jn)                                        \
+                        acc[jm][jn] = __builtin_amdgcn_mfma_f32_16x16x4f32(AC[jm][s_], BC[jn][s_], acc[jm][jn],  \
+                            0, 0, 0);                                                                            \
+        }                                                                                                        \
+        dma_step_schedule<TL::MB + TL::NB, TL::MB * TL::NB * (TL::BF16 ? 1 : 4)>();                              \
         if (kt_ + STAGES - 1 < nk) issue((kt_ + STAGES - 1) % STAGES, (kt_ + STAGES - 1) * BK);                  \
         stage_ready(kt_ + 2, nk - 1 < kt_ + STAGES - 1 ? nk - 1 : kt_ + STAGES - 1);                            \
     }
@@ -459,8 +477,9 @@ GemmPlan plan_gemm(bool bf16, int M, int K, int N, const void* x, const void* w)
     p.vec = (K % (bf16 ? 8 : 4) == 0) && (((size_t)x | (size_t)w) % 16 == 0);
     // LDS-DMA path: bf16, whole 16-byte K groups, each operand addressable with 31-bit
     // byte offsets (the buffer resource's out-of-range offset must lie past its end).
-    p.dma = bf16 && p.vec && K % 64 == 0 && (long long)M * K * 2 < 0x7FFF0000LL &&
-            (long long)N * K * 2 < 0x7FFF0000LL;
+    const long long esz = bf16 ? 2 : 4;
+    p.dma = p.vec && K % (bf16 ? 64 : 32) == 0 && (long long)M * K * esz < 0x7FFF0000LL &&
+            (long long)N * K * esz < 0x7FFF0000LL;
     p.part_bytes = (size_t)M * p.tilesN * sizeof(float2);
     return p;
 }
@@ -471,10 +490,15 @@ hipError_t launch_gemm_lse(const GemmPlan& p, const void* x, const void* w, cons
     float2* part = (float2*)workspace;
     if (timer) timer->begin("gemm_lse_partials", stream);
     hipError_t e;
-    if (p.dma) {
+    if (p.dma && p.bf16) {
         hipLaunchKernelGGL((gemm_lse_partials_dma<GTileD, kDmaStages>), dim3((unsigned)(p.tilesM * p.tilesN)),
                            dim3(GTileD::NT), 0, stream, (const unsigned short*)x, (const unsigned short*)w, b, part,
                            p.M, p.K, p.N, scale, cmin, cmax, p.tilesN);
+        e = hipGetLastError();
+    } else if (p.dma) {
+        hipLaunchKernelGGL((gemm_lse_partials_dma<GTileDF, kDmaStages>), dim3((unsigned)(p.tilesM * p.tilesN)),
+                           dim3(GTileDF::NT), 0, stream, (const float*)x, (const float*)w, b, part, p.M, p.K, p.N,
+                           scale, cmin, cmax, p.tilesN);
         e = hipGetLastError();
     } else {
         e = p.bf16 ? launch_partials<GTileH>(p, x, w, b, scale, cmin, cmax, part, stream)

@@ -46,7 +46,7 @@ struct GemmPlan {
     int BM, BN;
     int tilesM, tilesN;
     bool vec;                // K a multiple of a 16-byte group, 16-byte aligned rows: dwordx4 loads
-    bool dma;                // bf16 LDS-DMA kernel (vec, operands under 2 GiB)
+    bool dma;                // LDS-DMA kernel (vec, K a whole even number of 64-byte stages, operands under 2 GiB)
     size_t part_bytes;       // [M][tilesN] (max, sum) pairs
     size_t workspace_bytes() const { return part_bytes; }
 };
