@@ -31,8 +31,13 @@ def rand_case(seed, M, K, N, wb=None, dtype="f32"):
     return synth.gemm_inputs(dict(M=M, K=K, N=N, w_bound=wb, b_bound=wb, dtype=dtype), seed_cfg=2000 + seed)
 
 
+# K % 32 == 0 (fp32) / K % 64 == 0 (bf16) with 16-byte aligned operands takes the LDS-DMA
+# kernel; (300, 32, 385) is its shortest K (one pair of stages) with ragged rows and columns
+# over two tile rows and three tile columns, (513, 96, 400) three tile rows and an odd
+# number of stage pairs.
 @pytest.mark.parametrize("M,K,N", [(37, 19, 53), (1, 1, 1), (5, 4, 3), (128, 128, 128), (130, 260, 300),
-                                   (64, 1000, 129), (257, 33, 1000), (3, 4096, 6144)])
+                                   (64, 1000, 129), (257, 33, 1000), (3, 4096, 6144), (300, 32, 385),
+                                   (513, 96, 400)])
 @pytest.mark.parametrize("scale,cmin,cmax", [(4.0, -10.0, 10.0), (4.0, -0.25, 0.5), (-3.0, -1e30, 1e30)])
 def test_gemm_small_shapes(M, K, N, scale, cmin, cmax):
     X, W, b = rand_case(M + K + N, M, K, N)
@@ -44,7 +49,8 @@ def test_gemm_small_shapes(M, K, N, scale, cmin, cmax):
 
 
 @pytest.mark.parametrize("M,K,N", [(37, 19, 53), (1, 1, 1), (5, 8, 3), (128, 128, 128), (130, 264, 300),
-                                   (64, 1000, 129), (257, 33, 1000), (3, 4096, 6144), (300, 72, 385)])
+                                   (64, 1000, 129), (257, 33, 1000), (3, 4096, 6144), (300, 72, 385),
+                                   (300, 64, 385), (513, 192, 400)])
 @pytest.mark.parametrize("scale,cmin,cmax", [(4.0, -10.0, 10.0), (-3.0, -1e30, 1e30)])
 def test_gemm_bf16_small_shapes(M, K, N, scale, cmin, cmax):
     # K % 8 != 0 takes the element-wise load path, K % 8 == 0 the 16-byte one
@@ -53,6 +59,26 @@ def test_gemm_bf16_small_shapes(M, K, N, scale, cmin, cmax):
     ref, _ = oracle.gemm_lse_mish(X, W, b, scale, cmin, cmax)
     err = max_rel_err(got, ref)
     print(f"bf16 M={M} K={K} N={N} scale={scale} clamp=[{cmin},{cmax}] err={err:.3e}", flush=True)
+    assert err <= TOL_F32
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_gemm_unaligned_operands(dtype):
+    # operands starting one element past a 16-byte boundary: K would suit the DMA kernel,
+    # but the plan must fall back to the element-wise loads
+    M, K, N = 70, 128, 200
+    X, W, b = rand_case(7, M, K, N, dtype=dtype)
+    bf16 = dtype == "bf16"
+    def shifted(a):
+        d = to_device(np.concatenate([a.reshape(-1)[:1], a.reshape(-1)]), bf16)
+        return d[1:].view(a.shape)
+    xd, wd = shifted(X), shifted(W)
+    assert xd.data_ptr() % 16 != 0 and wd.data_ptr() % 16 != 0
+    out = fc.gemm_lse_mish(xd, wd, to_device(b), 4.0, -10.0, 10.0)
+    torch.cuda.synchronize()
+    ref, _ = oracle.gemm_lse_mish(X, W, b, 4.0, -10.0, 10.0)
+    err = max_rel_err(out.cpu().numpy()[:, 0], ref)
+    print(f"{dtype} unaligned M={M} K={K} N={N} err={err:.3e}", flush=True)
     assert err <= TOL_F32
 
 
