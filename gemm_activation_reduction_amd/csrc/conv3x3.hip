@@ -277,6 +277,14 @@ __global__ __launch_bounds__(TL::NT) __attribute__((amdgpu_waves_per_eu(TL::MINW
     const __amdgpu_buffer_rsrc_t wr = make_rsrc(wp, (unsigned)(nChunk * 9 * CoutPad * 64));
 
     // Nine shifted tap GEMMs over the chunk held in LDS.
+    // bf16 A fragments: the wave's blocks are 2 x 2 blocks from row wpi * WPB / CB, so each
+    // fragment address is one per-lane base plus an immediate. (Written through the block
+    // index wpi * WPB + j, the compiler kept a position per fragment in registers and
+    // multiplied it out per tap: 1.8 % slower. fp32 keeps that form: there the compiler
+    // already used one base per block, and the rewrite changed its register allocation
+    // for the worse.)
+    static_assert(TL::WPB % TL::CB == 0, "bf16: a wave's blocks are whole block rows");
+    const unsigned char* a_base = halo + (wpi * (TL::WPB / TL::CB) * TL::HP + i) * kRow + g * 16;
     auto compute_chunk = [&]() {
     #pragma unroll
         for (int tap = 0; tap < 9; ++tap) {
@@ -284,9 +292,13 @@ __global__ __launch_bounds__(TL::NT) __attribute__((amdgpu_waves_per_eu(TL::MINW
             u4 a[TL::WPB], b[TL::WOB];
     #pragma unroll
             for (int j = 0; j < TL::WPB; ++j) {
-                const int pb = wpi * TL::WPB + j;
-                const int pos = (pb_row(pb) + kh) * TL::HP + pb_col(pb) * 16 + i + kw;
-                a[j] = *(const u4*)(halo + pos * kRow + g * 16);
+                if constexpr (BF16) {
+                    a[j] = *(const u4*)(a_base + ((j / TL::CB + kh) * TL::HP + (j % TL::CB) * 16 + kw) * kRow);
+                } else {
+                    const int pb = wpi * TL::WPB + j;
+                    const int pos = (pb_row(pb) + kh) * TL::HP + pb_col(pb) * 16 + i + kw;
+                    a[j] = *(const u4*)(halo + pos * kRow + g * 16);
+                }
             }
     #pragma unroll
             for (int j = 0; j < TL::WOB; ++j) {
