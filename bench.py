@@ -198,6 +198,37 @@ def epilogue_bytes(spec) -> float:
     return 4.0 * (total + shape[0])
 
 
+def per_step_ms(step, n, torch, stream, flush=None):
+    """Per-step times (ms) from torch events on the launch stream. With `flush`, it runs
+    before each step's first event (outside the timed interval)."""
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    for a, b in evs:
+        if flush is not None:
+            flush()
+        a.record(stream)
+        step()
+        b.record(stream)
+    torch.cuda.synchronize()
+    return [a.elapsed_time(b) for a, b in evs]
+
+
+COLD_FLUSH_MIB = 512
+
+
+def warm_and_cold(step, steps, torch, dev):
+    """(median warm step ms, median cold step ms, cold steps). Cold: each step follows a
+    512 MiB read stream over a scratch buffer (a sum), which evicts L2 and the 256 MB MALL
+    with clean lines (inputs of up to ~256 MB otherwise stay in the MALL between steps; a
+    read + write stream would leave dirty lines whose write-back lands in the timed step)."""
+    stream = torch.cuda.current_stream()
+    warm = per_step_ms(step, steps, torch, stream)
+    flushbuf = torch.zeros(COLD_FLUSH_MIB << 18, dtype=torch.float32, device=dev)
+    ncold = min(steps, 20)
+    cold = per_step_ms(step, ncold, torch, stream, flush=lambda: flushbuf.sum())
+    del flushbuf
+    return float(np.median(warm)), float(np.median(cold)), ncold
+
+
 def bench_epilogue(args, name, spec, torch, fc, dev) -> int:
     """HBM-bound epilogue-only kernels: GB/s of algorithmic traffic against 8 TB/s."""
     print(f"bench: generating inputs for {name}", file=sys.stderr, flush=True)
@@ -237,11 +268,13 @@ def bench_epilogue(args, name, spec, torch, fc, dev) -> int:
     torch.cuda.synchronize()
     kms, kl = fc.fconv_profile_read(kernel)
     fc.fconv_profile(False)
+    med_ms, cold_ms, ncold = warm_and_cold(step, args.steps, torch, dev)
     ms_per_step = (t1 - t0) * 1e3 / args.steps
     kernel_ms = kms / max(1, kl)
     value = nbytes / (ms_per_step * 1e-3) / 1e9
     achieved = nbytes / (kernel_ms * 1e-3) / 1e9
-    print(f"bench: {ms_per_step:.4f} ms/step, {kernel} {kernel_ms:.4f} ms/launch, {achieved:.1f} GB/s",
+    print(f"bench: {ms_per_step:.4f} ms/step, {kernel} {kernel_ms:.4f} ms/launch, {achieved:.1f} GB/s; "
+          f"median step {med_ms:.4f} ms, cold-cache median {cold_ms:.4f} ms ({nbytes / (cold_ms * 1e-3) / 1e9:.1f} GB/s)",
           file=sys.stderr, flush=True)
     calibration_copies(args, torch, dev)
     cpu = None
@@ -274,6 +307,9 @@ def bench_epilogue(args, name, spec, torch, fc, dev) -> int:
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
         "config": {"workload": name, "shape": list(shape), "kind": kind},
+        "median_ms_per_step": round(med_ms, 5),
+        "cold": {"median_ms_per_step": round(cold_ms, 5), "value": round(nbytes / (cold_ms * 1e-3) / 1e9, 1),
+                 "unit": "GB/s", "steps": ncold, "flush_mib": COLD_FLUSH_MIB},
         "roofline": {"bound": "hbm", "kernel": kernel, "achieved": round(achieved, 1), "peak": HBM_GBPS,
                      "unit": "GB/s", "frac": round(achieved / HBM_GBPS, 4), "traffic": read_traffic(name, kernel),
                      "kernel_ms": round(kernel_ms, 5), "algorithmic_bytes": nbytes},
@@ -365,6 +401,8 @@ def main() -> int:
     kms, klaunches = fc.fconv_profile_read(kernel)
     others = {k: fc.fconv_profile_read(k) for k in ("pack_weights", "pool_finalize", "lse_merge_mish")}
     fc.fconv_profile(False)
+    # timed regions 3 and 4: per-step events with warm caches (median), then cold caches
+    med_ms, cold_ms, ncold = warm_and_cold(step, args.steps, torch, dev)
     ms_per_step = (t1 - t0) * 1e3 / args.steps
     ev_ms_per_step = ev0.elapsed_time(ev1) / args.steps
     kernel_ms = kms / max(1, klaunches)
@@ -376,7 +414,8 @@ def main() -> int:
         if nl:
             print(f"bench: {k} {ms / nl * 1e3:.2f} us/launch", file=sys.stderr, flush=True)
     print(f"bench: {ms_per_step:.4f} ms/step (events {ev_ms_per_step:.4f}), {kernel} {kernel_ms:.4f} ms/launch "
-          f"over {klaunches} launches, {achieved:.2f} TFLOP/s, {nbytes / (kernel_ms * 1e-3) / 1e9:.1f} GB/s algorithmic",
+          f"over {klaunches} launches, {achieved:.2f} TFLOP/s, {nbytes / (kernel_ms * 1e-3) / 1e9:.1f} GB/s algorithmic; "
+          f"median step {med_ms:.4f} ms, cold-cache median {cold_ms:.4f} ms ({flops / (cold_ms * 1e-3) / 1e12:.2f} TFLOP/s)",
           file=sys.stderr, flush=True)
 
     calibration_copies(args, torch, dev)
@@ -406,6 +445,9 @@ def main() -> int:
         "data": "synthetic",
         "config": cfg,
         "pct_mfma_peak": round(100.0 * value / peak, 2),
+        "median_ms_per_step": round(med_ms, 5),
+        "cold": {"median_ms_per_step": round(cold_ms, 5), "value": round(flops / (cold_ms * 1e-3) / 1e12, 3),
+                 "unit": "TFLOP/s", "steps": ncold, "flush_mib": COLD_FLUSH_MIB},
         "roofline": {"bound": "mfma", "kernel": kernel, "achieved": round(achieved, 3), "peak": peak,
                      "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": traffic,
                      "kernel_ms": round(kernel_ms, 5), "algorithmic_bytes": nbytes,
