@@ -135,3 +135,24 @@ def test_gemm_full_size_sampled_rows(name):
     lo, hi = spec["cmin"] + math.log(spec["N"]), spec["cmax"] + math.log(spec["N"])
     zz_lo, zz_hi = lo * lo * math.tanh(math.log1p(math.exp(lo))), hi * hi
     assert np.all(got >= min(zz_lo, 0.0) - 1e-3) and np.all(got <= zz_hi + 1e-3)
+
+
+@pytest.mark.parametrize("dtype,M", [("f32", 140000), ("bf16", 270000)])
+def test_gemm_operand_over_2gib(dtype, M):
+    # x of more than 2 GiB (but under 2^31 elements): too large for the LDS-DMA kernel's
+    # 31-bit buffer offsets, so the plan takes the register-staged kernel, whose row
+    # offsets are 64-bit. x repeats a 1024-row random block; rows sampled from the first
+    # block, the middle and the far end (byte offsets past 2^31) are checked.
+    K, N = 4096, 200
+    Xb, W, b = rand_case(11, 1024, K, N, dtype=dtype)
+    X = np.tile(Xb, (M // 1024 + 1, 1))[:M]
+    esz = 2 if dtype == "bf16" else 4
+    assert M * K * esz > 2 ** 31 and M * K < 2 ** 31
+    got = run_gemm(X, W, b)
+    rows = np.array([0, 1, 1023, M // 2, M - 1025, M - 2, M - 1])
+    ref, _ = oracle.gemm_lse_mish(X[rows], W, b, 4.0, -10.0, 10.0)
+    err = max_rel_err(got[rows], ref)
+    print(f"{dtype} M={M} K={K} N={N} ({M * K * esz / 2 ** 30:.2f} GiB) sampled err={err:.3e}", flush=True)
+    assert err <= TOL_F32
+    # rows that repeat the same block row give the same result
+    assert np.array_equal(got[rows[1:3]], got[rows[1:3] + 1024 * 100])
