@@ -352,18 +352,17 @@ __global__ __launch_bounds__(TL::NT) void gemm_lse_partials_dma(
     // Waits until this wave's DMA of stage `st` has landed, allowing its DMA of the stages
     // issued after it (up to `last`) to stay in flight, then a bare barrier (not
     // __syncthreads, whose release fence would wait for every DMA in flight): afterwards
-    // stage st is in LDS for every wave, and every wave's earlier LDS reads are done.
-    // s_waitcnt immediates (gfx9 encoding: vmcnt bits [3:0] and [15:14], expcnt [6:4],
-    // lgkmcnt [11:8]; a field at its maximum is not waited on): lgkmcnt(0), then vmcnt(n).
-    // Issued through the builtin so the compiler's own wait insertion knows the counters
-    // drained.
+    // stage st is in LDS for every wave. s_waitcnt immediates (gfx9 encoding: vmcnt bits
+    // [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8]; a field at its maximum is not waited
+    // on): vmcnt(n) only. Issued through the builtin so the compiler's own wait insertion
+    // knows the counter drained.
     auto stage_ready = [&](int st, int last) {
         const int inflight = (last > st ? last - st : 0) * per_stage;
         __asm__ volatile("" ::: "memory");  // the LDS reads issued above stay above the wait
-        // lgkmcnt(0) on its own, unconditionally: were it only inside the branches below,
-        // the compiler's wait insertion would see a path around it and make the next
-        // step's first MFMA wait for LDS reads issued after this point.
-        __builtin_amdgcn_s_waitcnt(0xC07F);
+        // The fragment reads of the next stage are not waited for here: they stay in flight
+        // across the barrier, and the compiler waits for each register at its first MFMA.
+        // (Their buffer is next overwritten by the DMA issued two barriers later, after the
+        // MFMAs that consumed them; measured 1.8 % faster for bf16 than waiting here.)
         if (inflight >= 8) __builtin_amdgcn_s_waitcnt(0x0F78);
         else if (inflight >= 6) __builtin_amdgcn_s_waitcnt(0x0F76);
         else if (inflight >= 4) __builtin_amdgcn_s_waitcnt(0x0F74);
