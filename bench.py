@@ -323,7 +323,10 @@ def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    # the shader clock ramps up over the first ~30 back-to-back steps (measured on the 3x3
+    # GELU+pool fp32 workload: 0.64 ms falling to 0.55 ms per step), so the default warm-up
+    # covers the ramp
+    ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD,
                     choices=sorted(list(synth.CONV_WORKLOADS) + list(synth.GEMM_WORKLOADS)
                                    + list(synth.EPILOGUE_WORKLOADS)))
@@ -340,6 +343,10 @@ def main() -> int:
     import gemm_activation_reduction_amd as fc
 
     dev = torch.device("cuda:0")
+    # Everything runs on a stream of its own (default priority), as a serving loop would:
+    # on torch's default (null) stream every launch also synchronizes with the other
+    # blocking streams, which measured 2-5 % longer per step.
+    torch.cuda.set_stream(torch.cuda.Stream(device=dev))
     name = args.workload
     if name in synth.EPILOGUE_WORKLOADS:
         return bench_epilogue(args, name, synth.EPILOGUE_WORKLOADS[name], torch, fc, dev)
