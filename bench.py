@@ -1,6 +1,6 @@
 """Benchmark of the fused conv / GEMM-logsumexp library on one MI355X.
 
-    python bench.py [--steps K] [--warmup W] [--workload NAME] [--cpu-seconds S]
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--cpu-seconds S] [--cold-steps C]
 
 A step is one call of the fused operation (all of its kernels) on one batch of
 synthetic input already resident in HBM. The default workload is the fp32
@@ -215,18 +215,19 @@ def per_step_ms(step, n, torch, stream, flush=None):
 COLD_FLUSH_MIB = 512
 
 
-def warm_and_cold(step, steps, torch, dev):
+def warm_and_cold(step, steps, cold_steps, torch, dev):
     """(median warm step ms, median cold step ms, cold steps). Cold: each step follows a
     512 MiB read stream over a scratch buffer (a sum), which evicts L2 and the 256 MB MALL
     with clean lines (inputs of up to ~256 MB otherwise stay in the MALL between steps; a
     read + write stream would leave dirty lines whose write-back lands in the timed step)."""
     stream = torch.cuda.current_stream()
     warm = per_step_ms(step, steps, torch, stream)
+    if cold_steps <= 0:
+        return float(np.median(warm)), None, 0
     flushbuf = torch.zeros(COLD_FLUSH_MIB << 18, dtype=torch.float32, device=dev)
-    ncold = min(steps, 20)
-    cold = per_step_ms(step, ncold, torch, stream, flush=lambda: flushbuf.sum())
+    cold = per_step_ms(step, cold_steps, torch, stream, flush=lambda: flushbuf.sum())
     del flushbuf
-    return float(np.median(warm)), float(np.median(cold)), ncold
+    return float(np.median(warm)), float(np.median(cold)), cold_steps
 
 
 def bench_epilogue(args, name, spec, torch, fc, dev) -> int:
@@ -268,14 +269,15 @@ def bench_epilogue(args, name, spec, torch, fc, dev) -> int:
     torch.cuda.synchronize()
     kms, kl = fc.fconv_profile_read(kernel)
     fc.fconv_profile(False)
-    med_ms, cold_ms, ncold = warm_and_cold(step, args.steps, torch, dev)
+    med_ms, cold_ms, ncold = warm_and_cold(step, args.steps, args.cold_steps, torch, dev)
     ms_per_step = (t1 - t0) * 1e3 / args.steps
     kernel_ms = kms / max(1, kl)
     value = nbytes / (ms_per_step * 1e-3) / 1e9
     achieved = nbytes / (kernel_ms * 1e-3) / 1e9
+    cold_txt = (f", cold-cache median {cold_ms:.4f} ms ({nbytes / (cold_ms * 1e-3) / 1e9:.1f} GB/s)"
+                if ncold else "")
     print(f"bench: {ms_per_step:.4f} ms/step, {kernel} {kernel_ms:.4f} ms/launch, {achieved:.1f} GB/s; "
-          f"median step {med_ms:.4f} ms, cold-cache median {cold_ms:.4f} ms ({nbytes / (cold_ms * 1e-3) / 1e9:.1f} GB/s)",
-          file=sys.stderr, flush=True)
+          f"median step {med_ms:.4f} ms{cold_txt}", file=sys.stderr, flush=True)
     calibration_copies(args, torch, dev)
     cpu = None
     if args.cpu_seconds > 0:
@@ -309,7 +311,7 @@ def bench_epilogue(args, name, spec, torch, fc, dev) -> int:
         "config": {"workload": name, "shape": list(shape), "kind": kind},
         "median_ms_per_step": round(med_ms, 5),
         "cold": {"median_ms_per_step": round(cold_ms, 5), "value": round(nbytes / (cold_ms * 1e-3) / 1e9, 1),
-                 "unit": "GB/s", "steps": ncold, "flush_mib": COLD_FLUSH_MIB},
+                 "unit": "GB/s", "steps": ncold, "flush_mib": COLD_FLUSH_MIB} if ncold else None,
         "roofline": {"bound": "hbm", "kernel": kernel, "achieved": round(achieved, 1), "peak": HBM_GBPS,
                      "unit": "GB/s", "frac": round(achieved / HBM_GBPS, 4), "traffic": read_traffic(name, kernel),
                      "kernel_ms": round(kernel_ms, 5), "algorithmic_bytes": nbytes},
@@ -327,6 +329,8 @@ def main() -> int:
     # GELU+pool fp32 workload: 0.64 ms falling to 0.55 ms per step), so the default warm-up
     # covers the ramp
     ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--cold-steps", type=int, default=20,
+                    help="steps timed after evicting L2 and the MALL (0: skip)")
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD,
                     choices=sorted(list(synth.CONV_WORKLOADS) + list(synth.GEMM_WORKLOADS)
                                    + list(synth.EPILOGUE_WORKLOADS)))
@@ -409,7 +413,7 @@ def main() -> int:
     others = {k: fc.fconv_profile_read(k) for k in ("pack_weights", "pool_finalize", "lse_merge_mish")}
     fc.fconv_profile(False)
     # timed regions 3 and 4: per-step events with warm caches (median), then cold caches
-    med_ms, cold_ms, ncold = warm_and_cold(step, args.steps, torch, dev)
+    med_ms, cold_ms, ncold = warm_and_cold(step, args.steps, args.cold_steps, torch, dev)
     ms_per_step = (t1 - t0) * 1e3 / args.steps
     ev_ms_per_step = ev0.elapsed_time(ev1) / args.steps
     kernel_ms = kms / max(1, klaunches)
@@ -422,7 +426,8 @@ def main() -> int:
             print(f"bench: {k} {ms / nl * 1e3:.2f} us/launch", file=sys.stderr, flush=True)
     print(f"bench: {ms_per_step:.4f} ms/step (events {ev_ms_per_step:.4f}), {kernel} {kernel_ms:.4f} ms/launch "
           f"over {klaunches} launches, {achieved:.2f} TFLOP/s, {nbytes / (kernel_ms * 1e-3) / 1e9:.1f} GB/s algorithmic; "
-          f"median step {med_ms:.4f} ms, cold-cache median {cold_ms:.4f} ms ({flops / (cold_ms * 1e-3) / 1e12:.2f} TFLOP/s)",
+          f"median step {med_ms:.4f} ms"
+          + (f", cold-cache median {cold_ms:.4f} ms ({flops / (cold_ms * 1e-3) / 1e12:.2f} TFLOP/s)" if ncold else ""),
           file=sys.stderr, flush=True)
 
     calibration_copies(args, torch, dev)
@@ -454,7 +459,7 @@ def main() -> int:
         "pct_mfma_peak": round(100.0 * value / peak, 2),
         "median_ms_per_step": round(med_ms, 5),
         "cold": {"median_ms_per_step": round(cold_ms, 5), "value": round(flops / (cold_ms * 1e-3) / 1e12, 3),
-                 "unit": "TFLOP/s", "steps": ncold, "flush_mib": COLD_FLUSH_MIB},
+                 "unit": "TFLOP/s", "steps": ncold, "flush_mib": COLD_FLUSH_MIB} if ncold else None,
         "roofline": {"bound": "mfma", "kernel": kernel, "achieved": round(achieved, 3), "peak": peak,
                      "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": traffic,
                      "kernel_ms": round(kernel_ms, 5), "algorithmic_bytes": nbytes,
