@@ -156,3 +156,40 @@ def test_gemm_operand_over_2gib(dtype, M):
     assert err <= TOL_F32
     # rows that repeat the same block row give the same result
     assert np.array_equal(got[rows[1:3]], got[rows[1:3] + 1024 * 100])
+
+
+def test_concurrent_streams_bit_equal():
+    # three streams with different work enqueued interleaved (no synchronization between
+    # them): each stream has its own library workspace, so every result must equal the one
+    # computed alone on the default stream, bit for bit
+    import synth as sy
+    spec_a = dict(N=3, Cin=16, H=70, W=90, Cout=80, act=1, pool=1, dtype="f32", x_dist=("normal",),
+                  w_bound=1 / 12, b_bound=0.1)
+    spec_b = dict(N=2, Cin=40, H=40, W=48, Cout=64, act=2, pool=0, dtype="bf16", x_dist=("normal",),
+                  w_bound=0.05, b_bound=0.1)
+    xa, wa, ba = sy.conv_inputs(spec_a, seed_cfg=801)
+    xb, wb, bb = sy.conv_inputs(spec_b, seed_cfg=802)
+    X, W, b = rand_case(803, 300, 256, 700)
+    da = (to_device(xa), to_device(wa), to_device(ba))
+    db = (to_device(xb, True), to_device(wb, True), to_device(bb))
+    dg = (to_device(X), to_device(W), to_device(b))
+    ref_a = fc.conv_act_pool(*da, act="gelu", pool=True)
+    ref_b = fc.conv_act_pool(*db, act="mish2", pool=False)
+    ref_g = fc.gemm_lse_mish(*dg, 4.0, -10.0, 10.0)
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream() for _ in range(3)]
+    outs = {0: [], 1: [], 2: []}
+    for _ in range(4):
+        with torch.cuda.stream(streams[0]):
+            outs[0].append(fc.conv_act_pool(*da, act="gelu", pool=True, stream=streams[0]))
+        with torch.cuda.stream(streams[1]):
+            outs[1].append(fc.conv_act_pool(*db, act="mish2", pool=False, stream=streams[1]))
+        with torch.cuda.stream(streams[2]):
+            outs[2].append(fc.gemm_lse_mish(*dg, 4.0, -10.0, 10.0, stream=streams[2]))
+    torch.cuda.synchronize()
+    for o in outs[0]:
+        assert torch.equal(o, ref_a)
+    for o in outs[1]:
+        assert torch.equal(o, ref_b)
+    for o in outs[2]:
+        assert torch.equal(o, ref_g)
