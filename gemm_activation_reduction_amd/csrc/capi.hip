@@ -182,7 +182,7 @@ int conv_impl(const char* name, const void* x, const void* w, const float* b, in
         return fail(FCONV_EINVAL, fn + ": out overlaps an input");
 
     const bool bf16 = dt == FCONV_DT_BF16;
-    const fconv::ConvPlan plan = fast ? fconv::plan_conv(bf16, kind, pool, N, Cin, H, W, Cout)
+    const fconv::ConvPlan plan = fast ? fconv::plan_conv(bf16, kind, pool, N, Cin, H, W, Cout, x)
                                       : fconv::plan_conv_general(bf16, kind, pool, N, Cin, H, W, Cout, K, stride, pad);
     if (plan.grid() > 0x7FFFFFFFLL) return fail(FCONV_EUNSUPPORTED, fn + ": launch grid too large");
     // The kernels address one image of x, and the repacked weights, with 32-bit byte offsets.

@@ -11,6 +11,9 @@
 // second kernel sums the partials in a fixed order, so the result is deterministic
 // without atomics.
 //
+// bf16 with 256 or more output channels (and 16-byte halo loads) runs conv3x3_wide_bf16
+// instead: 256 oc per workgroup, weights streamed per tap into LDS by DMA (see there).
+//
 // The operation is the Conv2d -> activation (-> AdaptiveAvgPool2d(1)) chain of
 // the "Kimi-K2.6 l2_p67" and "Kimi-K2.6 l2_p4" POPCORNBENCH pages; the pages'
 // own kernels (shared-memory direct convolution on CUDA cores) are not followed.
@@ -434,6 +437,227 @@ __global__ __launch_bounds__(TL::NT) __attribute__((amdgpu_waves_per_eu(TL::MINW
 }
 
 
+// ---------------------------------------------------------------------------------
+// bf16, all of 256 output channels per workgroup ("wide"). The input halo of a pixel tile
+// is staged once for 256 channels instead of once per 64, and the weights stream tap by
+// tap from HBM/L2 into a ring of LDS slots by LDS DMA (buffer_load_dwordx4 ... lds), so
+// they take no registers, no LDS store instructions and no address arithmetic per chunk.
+// Tile: 4 output rows x 32 columns x 256 oc; 4 waves, each 2 x 2 pixel blocks x 8 oc
+// blocks (128 accumulator registers). A K step is one tap of one 32-channel chunk:
+// 32 MFMAs per wave. LDS: the halo (6 x 36 positions, 80-byte rows as in the narrow
+// kernel) and kWideSlots tap slots of 256 rows x 64 bytes. A wave's DMA fills 1 KB in lane
+// order (16 rows x 4 slots); slot s of a row with in-block index r holds K group
+// s ^ f(r), f(r) = ((r >> 1) ^ (r >> 3)) & 3, which keeps the B fragment reads (16 rows x
+// 4 groups) on distinct banks.
+// ---------------------------------------------------------------------------------
+using TileW = Tile<4, 32, 256, 2, 2, 2, 256>;
+constexpr int kWideSlots = 3;                  // tap slots: the DMA runs two taps ahead
+constexpr int kWideSlot = TileW::BN * 64;      // bytes per tap slot
+constexpr int kWideLds = kWideSlots * kWideSlot + TileW::HPOS * kRow;
+
+template <int ACT, bool POOL>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void conv3x3_wide_bf16(
+    const unsigned short* __restrict__ x, const unsigned short* __restrict__ wp, const float* __restrict__ bias,
+    float* __restrict__ dst, int Cin, int H, int W, int Cout, int CoutPad, int nChunk, int tilesH, int tilesW,
+    int ocTiles, int out_align) {
+    using TL = TileW;
+    constexpr int CK = Elem<true>::CK;
+    static_assert(TL::NT == 256 && TL::WPB == 4 && TL::WOB == 8 && TL::CB == 2, "wide tile shape");
+    __shared__ __attribute__((aligned(1024))) unsigned char smem[kWideLds];
+    unsigned char* ring = smem;
+    unsigned char* halo = smem + kWideSlots * kWideSlot;
+
+    int bid = xcd_contiguous_index(blockIdx.x, gridDim.x);
+    const int ot = bid % ocTiles; bid /= ocTiles;
+    const int tw = bid % tilesW; bid /= tilesW;
+    const int th = bid % tilesH;
+    const int n = bid / tilesH;
+    const int OH = H - 2, OW = W - 2;
+    const int oh0 = th * TL::TH, ow0 = tw * TL::TW, oc0 = ot * TL::BN;
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar DMA choices
+    const int g = lane >> 4, i = lane & 15;
+    const int wpi = wave % TL::WP, woi = wave / TL::WP;
+    const int row0 = wpi * (TL::WPB / TL::CB);  // the wave's blocks: rows row0, row0 + 1, two block columns
+
+    f4 acc[TL::WPB][TL::WOB];
+#pragma unroll
+    for (int c = 0; c < TL::WOB; ++c) {
+        const int oc = oc0 + (woi * TL::WOB + c) * 16 + i;
+        const float bv = oc < Cout ? bias[oc] : 0.0f;
+#pragma unroll
+        for (int a = 0; a < TL::WPB; ++a) acc[a][c] = f4{bv, bv, bv, bv};
+    }
+
+    const long long plane = (long long)H * W;
+    const __amdgpu_buffer_rsrc_t xr = make_rsrc(x + (long long)n * Cin * plane, (unsigned)(Cin * plane * 2));
+    const __amdgpu_buffer_rsrc_t wr = make_rsrc(wp, (unsigned)(nChunk * 9 * CoutPad * 64));
+
+    // DMA of K step s (chunk s / 9, tap s % 9) into slot s % kWideSlots: 16 instructions of
+    // 16 rows, 4 per wave. Lane l covers row l >> 2 of its block, physical slot l & 3, which
+    // holds K group (l & 3) ^ f(l >> 2).
+    const int dma_r = lane >> 2;
+    const int dma_grp = (lane & 3) ^ (((dma_r >> 1) ^ (dma_r >> 3)) & 3);
+    auto issue = [&](int s) {
+        const int slot = s % kWideSlots;
+        const int rowbase = s * CoutPad + oc0;  // [chunk][tap] row index: (chunk * 9 + tap) * CoutPad
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int ins = wave + 4 * q;
+            typedef __attribute__((address_space(3))) void lds_t;
+            lds_t* d = (lds_t*)(ring + slot * kWideSlot + ins * 1024);
+            const int off = ((rowbase + ins * 16 + dma_r) * 4 + dma_grp) * 16;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, d, 16, off, 0, 0, 0);
+        }
+    };
+    // fragment offsets: A from the halo as in the narrow bf16 kernel, B from a tap slot
+    const unsigned char* a_base = halo + (row0 * TL::HP + i) * kRow + g * 16;
+    const int b_off = (woi * TL::WOB * 16 + i) * 64 + 16 * (g ^ (((i >> 1) ^ (i >> 3)) & 3));
+
+    HaloVec<true, TL> hs;
+    const int nsteps = nChunk * 9;
+    hs.load(xr, H, W, Cin, 0, oh0, ow0, tid);
+    issue(0);
+    if (nsteps > 1) issue(1);
+    hs.store(halo, tid);
+    // step 0's DMA has landed for this wave (step 1's may still fly), and the halo stores are done
+    asm volatile("" ::: "memory");
+    if (nsteps > 1) __builtin_amdgcn_s_waitcnt(0x0074);  // vmcnt(4) lgkmcnt(0)
+    else __builtin_amdgcn_s_waitcnt(0x0070);             // vmcnt(0) lgkmcnt(0)
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+
+    // One K chunk (9 tap steps). NEXT: a later chunk follows, so its halo is loaded during
+    // taps 0-1 and stored after tap 8. Chunks before the last take NEXT = true and the last
+    // NEXT = false, which keeps every wait below a compile-time count (a runtime condition
+    // around the next halo's loads and store made the compiler drain all vector memory
+    // operations at the top of each chunk).
+    auto chunk = [&](const int c, auto next_tag) {
+        constexpr bool NEXT = decltype(next_tag)::value;
+#pragma unroll
+        for (int t = 0; t < 9; ++t) {
+            const int s = c * 9 + t;
+            // step s + 2 exists: always when a chunk follows; in the last chunk for taps 0-6
+            const bool ahead = NEXT || t + 2 < 9;
+            if (ahead) issue(s + 2);
+            if (NEXT && t == 0) hs.load(xr, H, W, Cin, (c + 1) * CK, oh0, ow0, tid);
+            const int kh = t / 3, kw = t % 3;
+            const unsigned char* bslot = ring + (s % kWideSlots) * kWideSlot + b_off;
+            u4 a[TL::WPB], b[TL::WOB];
+#pragma unroll
+            for (int j = 0; j < TL::WPB; ++j)
+                a[j] = *(const u4*)(a_base + ((j / TL::CB + kh) * TL::HP + (j % TL::CB) * 16 + kw) * kRow);
+#pragma unroll
+            for (int j = 0; j < TL::WOB; ++j) b[j] = *(const u4*)(bslot + j * 16 * 64);
+#pragma unroll
+            for (int jp = 0; jp < TL::WPB; ++jp)
+#pragma unroll
+                for (int jo = 0; jo < TL::WOB; ++jo)
+                    acc[jp][jo] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                        __builtin_bit_cast(bf16x8, a[jp]), __builtin_bit_cast(bf16x8, b[jo]), acc[jp][jo], 0, 0, 0);
+            // Before the barrier: this wave's reads of this step are done (the next step's DMA
+            // reuses the slot read here) and its DMA of step s + 1 has landed. Vector memory
+            // operations complete in order; those issued after step s + 1's DMA may stay in
+            // flight: step s + 2's DMA (4) and, in taps 0 and 1, the next chunk's 8 halo loads.
+            const int after = (ahead ? 4 : 0) + ((NEXT && t <= 1) ? 8 : 0);
+            asm volatile("" ::: "memory");
+            if (after == 12) __builtin_amdgcn_s_waitcnt(0x007C);      // vmcnt(12) lgkmcnt(0)
+            else if (after == 4) __builtin_amdgcn_s_waitcnt(0x0074);  // vmcnt(4) lgkmcnt(0)
+            else __builtin_amdgcn_s_waitcnt(0x0070);                  // vmcnt(0) lgkmcnt(0)
+            __builtin_amdgcn_s_barrier();
+            asm volatile("" ::: "memory");
+        }
+        if constexpr (NEXT) {
+            hs.store(halo, tid);  // every wave is past the chunk's last tap: the halo is free
+            asm volatile("" ::: "memory");
+            __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the stores are done
+            __builtin_amdgcn_s_barrier();
+            asm volatile("" ::: "memory");
+        }
+    };
+    for (int c = 0; c + 1 < nChunk; ++c) chunk(c, std::true_type{});
+    chunk(nChunk - 1, std::false_type{});
+
+    // Epilogue (accumulator layout: lane (g, i) register r holds pixel 4g + r of the pixel
+    // block and output channel i of the oc block).
+    const bool interior = oh0 + TL::TH <= OH && ow0 + TL::TW <= OW;  // uniform per workgroup
+    if constexpr (POOL) {
+        float psum[TL::WOB];
+#pragma unroll
+        for (int j = 0; j < TL::WOB; ++j) psum[j] = 0.0f;
+        if (interior) {
+#pragma unroll
+            for (int jp = 0; jp < TL::WPB; ++jp)
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+#pragma unroll
+                    for (int jo = 0; jo < TL::WOB; ++jo) psum[jo] += activate<ACT>(acc[jp][jo][r]);
+        } else {
+#pragma unroll
+            for (int jp = 0; jp < TL::WPB; ++jp) {
+                const int oh = oh0 + row0 + jp / TL::CB;
+                const int owb = ow0 + (jp % TL::CB) * 16 + 4 * g;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const bool valid = oh < OH && owb + r < OW;
+#pragma unroll
+                    for (int jo = 0; jo < TL::WOB; ++jo) {
+                        const float v = activate<ACT>(acc[jp][jo][r]);
+                        psum[jo] += valid ? v : 0.0f;
+                    }
+                }
+            }
+        }
+#pragma unroll
+        for (int jo = 0; jo < TL::WOB; ++jo) {
+            psum[jo] += __shfl_xor(psum[jo], 16, 64);
+            psum[jo] += __shfl_xor(psum[jo], 32, 64);
+        }
+        float* red = (float*)smem;  // the ring is free: the last step ended with a barrier
+        if (g == 0) {
+#pragma unroll
+            for (int jo = 0; jo < TL::WOB; ++jo) red[wpi * TL::BN + (woi * TL::WOB + jo) * 16 + i] = psum[jo];
+        }
+        __syncthreads();
+        const int nTiles = tilesH * tilesW;
+        {
+            float sum = 0.0f;
+#pragma unroll
+            for (int p = 0; p < TL::WP; ++p) sum += red[p * TL::BN + tid];
+            const int oc = oc0 + tid;
+            if (oc < Cout) dst[((long long)n * nTiles + th * tilesW + tw) * Cout + oc] = sum;
+        }
+    } else {
+#pragma unroll
+        for (int jp = 0; jp < TL::WPB; ++jp) {
+            const int oh = oh0 + row0 + jp / TL::CB;
+            const int owb = ow0 + (jp % TL::CB) * 16 + 4 * g;
+            if (oh >= OH) continue;
+#pragma unroll
+            for (int jo = 0; jo < TL::WOB; ++jo) {
+                const int oc = oc0 + (woi * TL::WOB + jo) * 16 + i;
+                if (oc >= Cout) continue;
+                float v[4];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) v[r] = activate<ACT>(acc[jp][jo][r]);
+                float* o = dst + (((long long)n * Cout + oc) * OH + oh) * OW + owb;
+                if ((OW & 3) == 0 && out_align >= 16 && owb + 3 < OW) {
+                    *(f4*)o = f4{v[0], v[1], v[2], v[3]};
+                } else if ((OW & 1) == 0 && out_align >= 8) {
+                    if (owb < OW) *(float2*)o = make_float2(v[0], v[1]);
+                    if (owb + 2 < OW) *(float2*)(o + 2) = make_float2(v[2], v[3]);
+                } else {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        if (owb + r < OW) o[r] = v[r];
+                }
+            }
+        }
+    }
+}
+
+
 template <bool BF16, int ACT, bool POOL, class TL>
 hipError_t launch_typed(const ConvPlan& p, const void* x, const void* wpk, const float* b,
                         float* dst, hipStream_t stream) {
@@ -465,17 +689,45 @@ hipError_t launch_act(const ConvPlan& p, const void* x, const void* wpk, const f
     }
 }
 
+template <int ACT, bool POOL>
+hipError_t launch_wide_typed(const ConvPlan& p, const void* x, const void* wpk, const float* b, float* dst,
+                             hipStream_t stream) {
+    hipLaunchKernelGGL((conv3x3_wide_bf16<ACT, POOL>), dim3((unsigned)p.grid()), dim3(TileW::NT), 0, stream,
+                       (const unsigned short*)x, (const unsigned short*)wpk, b, dst, p.Cin, p.H, p.W, p.Cout,
+                       p.CoutPad, p.nChunk, p.tilesH, p.tilesW, p.ocTiles,
+                       ((uintptr_t)dst % 16 == 0) ? 16 : ((uintptr_t)dst % 8 == 0 ? 8 : 4));
+    return hipGetLastError();
+}
+
+hipError_t launch_wide(const ConvPlan& p, const void* x, const void* wpk, const float* b, float* dst,
+                       hipStream_t stream) {
+    switch (p.act * 2 + p.pool) {
+        case 0: return launch_wide_typed<kActNone, false>(p, x, wpk, b, dst, stream);
+        case 1: return launch_wide_typed<kActNone, true>(p, x, wpk, b, dst, stream);
+        case 2: return launch_wide_typed<kActGelu, false>(p, x, wpk, b, dst, stream);
+        case 3: return launch_wide_typed<kActGelu, true>(p, x, wpk, b, dst, stream);
+        case 4: return launch_wide_typed<kActMish2, false>(p, x, wpk, b, dst, stream);
+        case 5: return launch_wide_typed<kActMish2, true>(p, x, wpk, b, dst, stream);
+        case 6: return launch_wide_typed<kActGeluTanh, false>(p, x, wpk, b, dst, stream);
+        case 7: return launch_wide_typed<kActGeluTanh, true>(p, x, wpk, b, dst, stream);
+        default: return hipErrorInvalidValue;
+    }
+}
+
 }  // namespace
 
-ConvPlan plan_conv(bool bf16, int act, int pool, int N, int Cin, int H, int W, int Cout) {
+ConvPlan plan_conv(bool bf16, int act, int pool, int N, int Cin, int H, int W, int Cout, const void* x) {
     ConvPlan p{};
     p.bf16 = bf16; p.act = act; p.pool = pool;
     p.N = N; p.Cin = Cin; p.H = H; p.W = W; p.Cout = Cout;
     p.OH = H - 2; p.OW = W - 2;
     p.KS = 3; p.stride = 1; p.pad = 0; p.general = false;
-    p.TH = bf16 ? TileB::TH : TileA::TH;
-    p.TW = bf16 ? TileB::TW : TileA::TW;
-    p.BN = bf16 ? TileB::BN : TileA::BN;
+    // bf16 with 256 or more output channels and 16-byte halo loads: the wide kernel
+    const bool vec = W % 8 == 0 && (uintptr_t)x % 16 == 0;
+    p.wide = bf16 && vec && Cout >= TileW::BN;
+    p.TH = p.wide ? TileW::TH : bf16 ? TileB::TH : TileA::TH;
+    p.TW = p.wide ? TileW::TW : bf16 ? TileB::TW : TileA::TW;
+    p.BN = p.wide ? TileW::BN : bf16 ? TileB::BN : TileA::BN;
     p.CK = bf16 ? Elem<true>::CK : Elem<false>::CK;
     p.tilesH = (p.OH + p.TH - 1) / p.TH;
     p.tilesW = (p.OW + p.TW - 1) / p.TW;
@@ -506,10 +758,12 @@ hipError_t launch_conv(const ConvPlan& p, const void* x, const void* w, const fl
     if (timer) timer->end("pack_weights", stream);
     if (e != hipSuccess) return e;
     float* dst = p.pool ? part : out;
-    if (timer) timer->begin("conv3x3_fused", stream);
-    e = p.bf16 ? launch_act<true, TileB>(p, x, wpk, b, dst, stream)
-               : launch_act<false, TileA>(p, x, wpk, b, dst, stream);
-    if (timer) timer->end("conv3x3_fused", stream);
+    const char* kname = p.wide ? "conv3x3_wide_bf16" : "conv3x3_fused";
+    if (timer) timer->begin(kname, stream);
+    e = p.wide   ? launch_wide(p, x, wpk, b, dst, stream)
+        : p.bf16 ? launch_act<true, TileB>(p, x, wpk, b, dst, stream)
+                 : launch_act<false, TileA>(p, x, wpk, b, dst, stream);
+    if (timer) timer->end(kname, stream);
     if (e != hipSuccess || !p.pool) return e;
     if (timer) timer->begin("pool_finalize", stream);
     hipLaunchKernelGGL(pool_finalize, dim3((unsigned)p.N, (unsigned)((p.Cout + 63) / 64)), dim3(256), 0, stream,

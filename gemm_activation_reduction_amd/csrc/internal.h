@@ -21,6 +21,7 @@ struct ConvPlan {
     int OH, OW;
     int KS, stride, pad;     // kernel size, stride, zero padding (3, 1, 0 on the 3x3 valid path)
     bool general;            // planned for the general-geometry kernel
+    bool wide;               // 3x3 bf16: 256 oc per workgroup, weights by LDS DMA
     int TH, TW, BN, CK;      // output tile rows/cols, oc per workgroup, channels per K chunk
     int tilesH, tilesW, ocTiles, nChunk, CoutPad;
     size_t wpack_bytes;      // repacked weights [nChunk][KS * KS][CoutPad][CK]
@@ -29,7 +30,7 @@ struct ConvPlan {
     long long grid() const { return (long long)N * tilesH * tilesW * ocTiles; }
 };
 
-ConvPlan plan_conv(bool bf16, int act, int pool, int N, int Cin, int H, int W, int Cout);
+ConvPlan plan_conv(bool bf16, int act, int pool, int N, int Cin, int H, int W, int Cout, const void* x);
 hipError_t launch_conv(const ConvPlan& p, const void* x, const void* w, const float* b,
                        float* out, void* workspace, hipStream_t stream, KernelTimer* timer);
 

@@ -175,7 +175,7 @@ int fconv_release(void);
  * outstanding events and clears the accumulated totals.
  * fconv_profile_read(kernel, &ms, &launches) waits for the recorded events and returns
  * the summed event time in milliseconds and the number of launches of `kernel` since
- * the last fconv_profile() call. Kernel names: "pack_weights", "conv3x3_fused",
+ * the last fconv_profile() call. Kernel names: "pack_weights", "conv3x3_fused", "conv3x3_wide_bf16",
  * "conv_general_fused", "pool_finalize", "gemm_lse_partials", "lse_merge_mish", "act_pool_map", "act_elementwise",
  * "scale_clamp_lse". Unknown names read as zero.
  * Returns FCONV_EINVAL for a null argument, FCONV_EHIP if an event wait fails.

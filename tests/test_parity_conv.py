@@ -211,3 +211,46 @@ def test_conv_image_near_the_32bit_offset_limit():
     err = max_rel_err(got, ref)
     print(f"near-limit image: sampled err={err:.3e}", flush=True)
     assert err <= TOL_F32
+
+
+# bf16 with Cout >= 256 and 16-byte halo loads runs the wide kernel (256 oc per workgroup,
+# weights streamed per tap by LDS DMA): one to four chunks with ragged channel tails,
+# ragged tile rows and columns, one, two and ragged oc tiles.
+WIDE_SHAPES = [
+    (1, 32, 10, 40, 256),   # one chunk, exactly one oc tile, 2 x 2 tiles (ragged columns)
+    (2, 40, 14, 48, 300),   # two chunks (8-channel tail), two oc tiles (44-channel tail)
+    (1, 128, 9, 32, 512),   # four chunks, two full oc tiles, a ragged tile row
+    (1, 3, 6, 16, 256),     # a 3-channel chunk, a tile of 4 x 14 outputs
+    (1, 96, 34, 64, 256),   # three chunks, 8 tile rows
+]
+
+
+@pytest.mark.parametrize("act", [fc.ACT_NONE, fc.ACT_GELU, fc.ACT_MISH2, fc.ACT_GELU_TANH])
+@pytest.mark.parametrize("pool", [0, 1])
+@pytest.mark.parametrize("shape", WIDE_SHAPES)
+def test_conv_wide_bf16_full_compare(shape, pool, act):
+    x, w, b = rand_case(hash(shape) % 991 + 7, *shape, bf16=True)
+    got = run_conv(x, w, b, act, pool, True)
+    ref = oracle.conv_act_pool(x, w, b, act, pool)
+    err = max_rel_err(got, ref)
+    print(f"wide shape={shape} pool={pool} act={act} err={err:.3e}", flush=True)
+    # bf16 products are exact in fp32 and accumulate in fp32: the fp32 bound applies
+    assert err <= TOL_F32
+
+
+@pytest.mark.parametrize("shape", [(2, 40, 14, 48, 300), (1, 96, 34, 64, 256)])
+def test_conv_wide_matches_narrow_full_map(shape):
+    # An x that starts 2 bytes past a 16-byte boundary takes the narrow kernel's element-wise
+    # halo path; both kernels accumulate chunk by chunk and tap by tap from the bias, so the
+    # full output maps agree bit for bit.
+    x, w, b = rand_case(hash(shape) % 983 + 3, *shape, bf16=True)
+    xd = to_device(x, True)
+    flat = torch.empty(xd.numel() + 1, dtype=torch.bfloat16, device=xd.device)
+    flat[1:] = xd.reshape(-1)
+    xu = flat[1:].view(xd.shape)
+    assert xd.data_ptr() % 16 == 0 and xu.data_ptr() % 16 != 0
+    wd, bd = to_device(w, True), to_device(b)
+    o_wide = fc.conv_act_pool(xd, wd, bd, act="mish2", pool=False)
+    o_narrow = fc.conv_act_pool(xu, wd, bd, act="mish2", pool=False)
+    torch.cuda.synchronize()
+    assert torch.equal(o_wide, o_narrow)
