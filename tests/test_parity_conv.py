@@ -238,7 +238,34 @@ def test_conv_wide_bf16_full_compare(shape, pool, act):
     assert err <= TOL_F32
 
 
-@pytest.mark.parametrize("shape", [(2, 40, 14, 48, 300), (1, 96, 34, 64, 256)])
+# Grids of more wide workgroups than the device holds at once (two per CU), so slots are
+# refilled and the XCD-contiguous tile numbering covers a count that is not a multiple of
+# the resident set: 1280 tiles with one 3-channel chunk; 768 tiles with two chunks, two oc
+# tiles and ragged tile rows and columns.
+WIDE_LARGE_GRID = [
+    (40, 3, 66, 66, 256, "gelu", 1),
+    (24, 40, 34, 40, 300, "mish2", 0),
+    (24, 40, 34, 40, 300, "gelu_tanh", 1),
+]
+
+
+@pytest.mark.parametrize("N,Cin,H,W,Cout,act,pool", WIDE_LARGE_GRID)
+def test_conv_wide_large_grid(N, Cin, H, W, Cout, act, pool):
+    x, w, b = rand_case(N * 7 + Cin + W, N, Cin, H, W, Cout, bf16=True)
+    tiles = N * ((H - 2 + 3) // 4) * ((W - 2 + 31) // 32) * ((Cout + 255) // 256)
+    assert tiles > 2 * torch.cuda.get_device_properties(0).multi_processor_count
+    xd, wd, bd = to_device(x, True), to_device(w, True), to_device(b)
+    got = fc.conv_act_pool(xd, wd, bd, act=act, pool=bool(pool))
+    torch.cuda.synchronize()
+    ref = oracle.conv_act_pool(x, w, b, {"gelu": fc.ACT_GELU, "mish2": fc.ACT_MISH2,
+                                         "gelu_tanh": fc.ACT_GELU_TANH}[act], pool)
+    err = max_rel_err(got.cpu().numpy(), ref)
+    print(f"wide large grid N={N} Cin={Cin} H={H} W={W} Cout={Cout} act={act} pool={pool} tiles={tiles} "
+          f"err={err:.3e}", flush=True)
+    assert err <= TOL_F32
+
+
+@pytest.mark.parametrize("shape", [(2, 40, 14, 48, 300), (1, 96, 34, 64, 256), (24, 40, 34, 40, 300)])
 def test_conv_wide_matches_narrow_full_map(shape):
     # An x that starts 2 bytes past a 16-byte boundary takes the narrow kernel's element-wise
     # halo path; both kernels accumulate chunk by chunk and tap by tap from the bias, so the
