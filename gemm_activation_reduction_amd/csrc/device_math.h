@@ -13,6 +13,15 @@ __device__ __forceinline__ float fast_exp(float v) {
     return __builtin_amdgcn_exp2f(v * 1.4426950408889634f);
 }
 
+// max(v, 0) and min(v, 20) as one v_med3_f32 each. On an MFMA accumulator fmaxf / fminf also
+// emit a canonicalizing v_max_f32 v, v (the compiler cannot tell the value is not a
+// signalling NaN), one more VALU instruction per output in every epilogue; with an infinite
+// bound the compiler turns the med3 back into that pair, so the bounds are +-FLT_MAX. Equal to
+// max / min for every finite v.
+constexpr float kFltMax = 3.402823466e38f;
+__device__ __forceinline__ float relu(float v) { return __builtin_amdgcn_fmed3f(v, 0.0f, kFltMax); }
+__device__ __forceinline__ float min20(float v) { return __builtin_amdgcn_fmed3f(v, -kFltMax, 20.0f); }
+
 // Exact-form GELU, 0.5 v (1 + erf(v / sqrt 2)) = v Phi(v) ("Kimi-K2.6 l2_p67" page:
 // PyTorch's default approximate='none' form, not the tanh approximation).
 // erfc is evaluated with the rational approximation of Abramowitz & Stegun, Handbook of
@@ -31,7 +40,7 @@ __device__ __forceinline__ float gelu_erf(float v) {
     p = fmaf(t, p, 0.127414796f);
     const float e = __builtin_amdgcn_exp2f(v * (v * -0.72134752044448170f));  // e^{-v^2/2}
     const float h = (t * p) * e;
-    return fmaf(-av, h, fmaxf(v, 0.0f));
+    return fmaf(-av, h, relu(v));
 }
 
 // Tanh-approximation GELU, 0.5 v (1 + tanh(u)), u = sqrt(2/pi) (v + 0.044715 v^3) (the
@@ -50,7 +59,7 @@ __device__ __forceinline__ float gelu_tanh(float v) {
 // to fp32 precision (2 / (q + 2) < 1e-17), so the result is v; for very negative v, q
 // underflows to 0 and mish(v) -> 0 as the exact function does.
 __device__ __forceinline__ float mish_f32(float v) {
-    const float t = fast_exp(fminf(v, 20.0f));
+    const float t = fast_exp(min20(v));
     const float q = t * (t + 2.0f);
     return v * (q * __builtin_amdgcn_rcpf(q + 2.0f));
 }
