@@ -340,8 +340,8 @@ def main() -> int:
                     help="after timing, run plain device copies of this size (HBM counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
-              "the multi-GPU sharding is described in DESIGN.md but not launched", file=sys.stderr)
+        print(f"bench.py: runs on one GPU only (asked for --gpus {args.gpus}); "
+              "sharding the work over several GPUs is not implemented", file=sys.stderr)
         return 2
 
     import torch

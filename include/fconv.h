@@ -33,7 +33,7 @@ extern "C" {
 enum {
     FCONV_OK = 0,
     FCONV_EINVAL = -1,       /* bad argument; nothing was enqueued                   */
-    FCONV_EUNSUPPORTED = -2, /* valid request this build does not implement          */
+    FCONV_EUNSUPPORTED = -2, /* valid request the library does not implement         */
     FCONV_EHIP = -3,         /* a HIP runtime call or kernel launch failed           */
     FCONV_ENOMEM = -4        /* the workspace could not be allocated                 */
 };
