@@ -448,12 +448,24 @@ __global__ __launch_bounds__(TL::NT) __attribute__((amdgpu_waves_per_eu(TL::MINW
 // kernel) and kWideSlots tap slots of 256 rows x 64 bytes. A wave's DMA fills 1 KB in lane
 // order (16 rows x 4 slots); slot s of a row with in-block index r holds K group
 // s ^ f(r), f(r) = ((r >> 1) ^ (r >> 3)) & 3, which keeps the B fragment reads (16 rows x
-// 4 groups) on distinct banks.
+// 4 groups) on distinct banks. The next chunk's halo also arrives by LDS DMA, into a raw
+// staging area, and is transposed LDS to LDS at the chunk boundary. So every vector memory
+// operation in the main loop is a DMA at a fixed place in program order, and the vmcnt waits
+// below, which count them, hold whatever the compiler does with other loads. (Counting
+// ordinary halo loads was not safe: the compiler may move a load from the read-only input
+// across the barriers, which left the last DMA instruction of a step unwaited.)
 // ---------------------------------------------------------------------------------
 using TileW = Tile<4, 32, 256, 2, 2, 2, 256>;
 constexpr int kWideSlots = 3;                  // tap slots: the DMA runs two taps ahead
 constexpr int kWideSlot = TileW::BN * 64;      // bytes per tap slot
-constexpr int kWideLds = kWideSlots * kWideSlot + TileW::HPOS * kRow;
+// Raw (NCHW-order) staging of the next chunk's halo, filled by LDS DMA: 16-byte runs of 8
+// pixels for (channel, halo row, column group 0-3), then 4-byte runs for halo columns 32-33
+// of each (channel, halo row), padded to one 256-lane block.
+constexpr int kRawA = 12 * 1024;
+constexpr int kRawB = 1024;
+constexpr int kWideLds = kWideSlots * kWideSlot + TileW::HPOS * kRow + kRawA + kRawB;
+static_assert(TileW::HR == 6 && TileW::HC == 34 && Elem<true>::CK == 32, "raw halo staging covers 32 x 6 x 34");
+static_assert(2 * kWideLds <= 160 * 1024, "two wide workgroups per CU");
 
 template <int ACT, bool POOL>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void conv3x3_wide_bf16(
@@ -466,6 +478,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void c
     __shared__ __attribute__((aligned(1024))) unsigned char smem[kWideLds];
     unsigned char* ring = smem;
     unsigned char* halo = smem + kWideSlots * kWideSlot;
+    unsigned char* raw = halo + TL::HPOS * kRow;
 
     int bid = xcd_contiguous_index(blockIdx.x, gridDim.x);
     const int ot = bid % ocTiles; bid /= ocTiles;
@@ -515,24 +528,72 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void c
     const unsigned char* a_base = halo + (row0 * TL::HP + i) * kRow + g * 16;
     const int b_off = (woi * TL::WOB * 16 + i) * 64 + 16 * (g ^ (((i >> 1) ^ (i >> 3)) & 3));
 
-    HaloVec<true, TL> hs;
+    // Halo DMA of the chunk starting at channel c0 into the raw staging area: 12 instructions
+    // of 16-byte runs and 4 of 4-byte runs, 4 per wave (3 + 1). Raw 16-byte entry
+    // e * 96 + (r * 4 + cg) * 4 + q holds channel c0 + 8q + e, halo row r, pixels 8cg..8cg+7;
+    // 4-byte entry e * 24 + r * 4 + q holds its pixels 32-33. Channels, rows and 8-pixel groups
+    // outside x read as zero (W is a multiple of 8, so a group is wholly in or out).
+    auto halo_issue = [&](int c0) {
+        typedef __attribute__((address_space(3))) void lds_t;
+#pragma unroll
+        for (int k = 0; k < 3; ++k) {
+            const int ia = wave + 4 * k;
+            const int ei = ia * 64 + lane;
+            const int e = ei / 96, rem = ei % 96;
+            const int q = rem & 3, cg = (rem >> 2) & 3, r = rem >> 4;
+            const int ch = c0 + 8 * q + e, ih = oh0 + r, iw = ow0 + 8 * cg;
+            const int off = (ch < Cin && ih < H && iw < W) ? ((ch * H + ih) * W + iw) * 2 : kOOB;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (lds_t*)(raw + ia * 1024), 16, off, 0, 0, 0);
+        }
+        {
+            const int ei = wave * 64 + lane;  // 192 entries; lanes 192-255 pad
+            const int e = ei / 24, rem = ei % 24;
+            const int q = rem & 3, r = rem >> 2;
+            const int ch = c0 + 8 * q + e, ih = oh0 + r, iw = ow0 + 32;
+            const int off = (ei < 192 && ch < Cin && ih < H && iw < W) ? ((ch * H + ih) * W + iw) * 2 : kOOB;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (lds_t*)(raw + kRawA + wave * 256), 4, off, 0, 0, 0);
+        }
+    };
+    // Raw staging -> channel-minor halo rows (the layout the A fragments read): item
+    // (channel group q, column group cg, halo row r) gathers its 8 channels' runs and
+    // writes them transposed, as the register-staged narrow kernel does.
+    auto halo_transpose = [&]() {
+        HaloVec<true, TL> hv;
+        int q, cg, r;
+        HaloVec<true, TL>::item(tid, q, cg, r);
+        if (tid < HaloVec<true, TL>::ITEMS) {
+            if (cg < 4) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) hv.v[0][e] = *(const u4*)(raw + (e * 96 + (r * 4 + cg) * 4 + q) * 16);
+            } else {
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    hv.v[0][e] = u4{*(const unsigned*)(raw + kRawA + (e * 24 + r * 4 + q) * 4), 0u, 0u, 0u};
+            }
+            hv.store(halo, tid);
+        }
+    };
+    static_assert(HaloVec<true, TL>::PER == 1 && HaloVec<true, TL>::NCG == 5, "one transpose item per thread");
+
     const int nsteps = nChunk * 9;
-    hs.load(xr, H, W, Cin, 0, oh0, ow0, tid);
+    halo_issue(0);
     issue(0);
     if (nsteps > 1) issue(1);
-    hs.store(halo, tid);
-    // step 0's DMA has landed for this wave (step 1's may still fly), and the halo stores are done
+    // the halo and step 0 have landed for this wave (step 1's DMA may fly)
     asm volatile("" ::: "memory");
     if (nsteps > 1) __builtin_amdgcn_s_waitcnt(0x0074);  // vmcnt(4) lgkmcnt(0)
     else __builtin_amdgcn_s_waitcnt(0x0070);             // vmcnt(0) lgkmcnt(0)
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
+    halo_transpose();
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the halo stores are done
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
 
-    // One K chunk (9 tap steps). NEXT: a later chunk follows, so its halo is loaded during
-    // taps 0-1 and stored after tap 8. Chunks before the last take NEXT = true and the last
-    // NEXT = false, which keeps every wait below a compile-time count (a runtime condition
-    // around the next halo's loads and store made the compiler drain all vector memory
-    // operations at the top of each chunk).
+    // One K chunk (9 tap steps). NEXT: a later chunk follows, so its halo DMA is sent in tap 0
+    // and transposed after tap 8. Chunks before the last take NEXT = true and the last
+    // NEXT = false, which keeps every wait below a compile-time count.
     auto chunk = [&](const int c, auto next_tag) {
         constexpr bool NEXT = decltype(next_tag)::value;
 #pragma unroll
@@ -541,7 +602,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void c
             // step s + 2 exists: always when a chunk follows; in the last chunk for taps 0-6
             const bool ahead = NEXT || t + 2 < 9;
             if (ahead) issue(s + 2);
-            if (NEXT && t == 0) hs.load(xr, H, W, Cin, (c + 1) * CK, oh0, ow0, tid);
+            if (NEXT && t == 0) halo_issue((c + 1) * CK);
             const int kh = t / 3, kw = t % 3;
             const unsigned char* bslot = ring + (s % kWideSlots) * kWideSlot + b_off;
             u4 a[TL::WPB], b[TL::WOB];
@@ -558,20 +619,21 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void c
                         __builtin_bit_cast(bf16x8, a[jp]), __builtin_bit_cast(bf16x8, b[jo]), acc[jp][jo], 0, 0, 0);
             // Before the barrier: this wave's reads of this step are done (the next step's DMA
             // reuses the slot read here) and its DMA of step s + 1 has landed. Vector memory
-            // operations complete in order; those issued after step s + 1's DMA may stay in
-            // flight: step s + 2's DMA (4) and, in taps 0 and 1, the next chunk's 8 halo loads.
-            const int after = (ahead ? 4 : 0) + ((NEXT && t <= 1) ? 8 : 0);
+            // operations complete in order; the DMA instructions sent after step s + 1's may stay
+            // in flight: step s + 2's (4) and, in taps 0 and 1, the next chunk's halo (4). The
+            // halo has landed by the end of tap 2, long before its transpose after tap 8.
+            const int after = (ahead ? 4 : 0) + ((NEXT && t <= 1) ? 4 : 0);
             asm volatile("" ::: "memory");
-            if (after == 12) __builtin_amdgcn_s_waitcnt(0x007C);      // vmcnt(12) lgkmcnt(0)
+            if (after == 8) __builtin_amdgcn_s_waitcnt(0x0078);       // vmcnt(8) lgkmcnt(0)
             else if (after == 4) __builtin_amdgcn_s_waitcnt(0x0074);  // vmcnt(4) lgkmcnt(0)
             else __builtin_amdgcn_s_waitcnt(0x0070);                  // vmcnt(0) lgkmcnt(0)
             __builtin_amdgcn_s_barrier();
             asm volatile("" ::: "memory");
         }
         if constexpr (NEXT) {
-            hs.store(halo, tid);  // every wave is past the chunk's last tap: the halo is free
+            halo_transpose();  // every wave is past the chunk's last tap: the halo is free
             asm volatile("" ::: "memory");
-            __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the stores are done
+            __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the raw reads and halo stores are done
             __builtin_amdgcn_s_barrier();
             asm volatile("" ::: "memory");
         }

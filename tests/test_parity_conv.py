@@ -165,6 +165,42 @@ def test_conv_full_size_mish2_full_output_sampled():
     assert err <= TOL_F32
 
 
+@pytest.mark.parametrize("act", ["none", "gelu"])
+def test_conv_wide_full_map_repeatable_at_workload_size(act):
+    # The 16 x 128 x 128^2 -> 256 bf16 inputs with the full (16, 256, 126, 126) map written:
+    # eight launches in a row must agree bit for bit, and sampled outputs (weighted towards
+    # the oc range whose weight rows the last DMA instruction of a K step fills) must match
+    # the oracle. A wait that let a wave pass a barrier before its last DMA had landed made
+    # about half of such launches wrong in one 16-channel block of one wave.
+    name = "conv_gelu_pool_bf16"
+    spec = synth.CONV_WORKLOADS[name]
+    x, w, b = workload_conv_inputs(name)
+    xd, wd, bd = to_device(x, True), to_device(w, True), to_device(b)
+    code = {"none": fc.ACT_NONE, "gelu": fc.ACT_GELU}[act]
+    print(f"{name} full map act={act}: running GPU", flush=True)
+    first = fc.conv_act_pool(xd, wd, bd, act=code, pool=False)
+    out = torch.empty_like(first)
+    s = torch.cuda.current_stream()
+    same = 0
+    for _ in range(8):
+        out.fill_(float("nan"))
+        fc.conv_act_pool(xd, wd, bd, act=code, pool=False, out=out, stream=s)
+        same += int(torch.equal(out, first))
+    torch.cuda.synchronize()
+    N, Cout, OH, OW = first.shape
+    r = np.random.default_rng(11)
+    cnt = 6000
+    n, oh, ow = r.integers(0, N, cnt), r.integers(0, OH, cnt), r.integers(0, OW, cnt)
+    oc = np.where(r.random(cnt) < 0.5, r.integers(192, 256, cnt), r.integers(0, Cout, cnt))
+    idx = [torch.from_numpy(a.astype(np.int64)).cuda() for a in (n, oc, oh, ow)]
+    got = first[idx[0], idx[1], idx[2], idx[3]].cpu().numpy()
+    ref = oracle.conv_point_sample(x, w, b, code, n, oc, oh, ow)
+    err = max_rel_err(got, ref)
+    print(f"{name} full map act={act}: {same} of 8 repeats bit-equal, sampled err={err:.3e}", flush=True)
+    assert same == 8
+    assert err <= TOL_F32
+
+
 def test_conv_pool_repeated_calls_with_changing_shapes():
     # Calls share the library's cached workspace (repacked weights, pool partials), which
     # grows on demand; every call must be right whatever shape the previous one had.
