@@ -258,6 +258,8 @@ WIDE_SHAPES = [
     (1, 128, 9, 32, 512),   # four chunks, two full oc tiles, a ragged tile row
     (1, 3, 6, 16, 256),     # a 3-channel chunk, a tile of 4 x 14 outputs
     (1, 96, 34, 64, 256),   # three chunks, 8 tile rows
+    (1, 33, 8, 8, 256),     # the narrowest vector-path image (one 8-pixel group), a 1-channel tail chunk
+    (3, 65, 11, 24, 257),   # a 1-channel tail chunk, a second oc tile of one channel, 3 images
 ]
 
 
