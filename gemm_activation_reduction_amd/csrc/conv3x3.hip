@@ -444,11 +444,16 @@ __global__ __launch_bounds__(TL::NT) __attribute__((amdgpu_waves_per_eu(TL::MINW
 // they take no registers, no LDS store instructions and no address arithmetic per chunk.
 // Tile: 4 output rows x 32 columns x 256 oc; 4 waves, each 2 x 2 pixel blocks x 8 oc
 // blocks (128 accumulator registers). A K step is one tap of one 32-channel chunk:
-// 32 MFMAs per wave. LDS: the halo (6 x 36 positions, 80-byte rows as in the narrow
-// kernel) and kWideSlots tap slots of 256 rows x 64 bytes. A wave's DMA fills 1 KB in lane
-// order (16 rows x 4 slots); slot s of a row with in-block index r holds K group
-// s ^ f(r), f(r) = ((r >> 1) ^ (r >> 3)) & 3, which keeps the B fragment reads (16 rows x
-// 4 groups) on distinct banks. The next chunk's halo also arrives by LDS DMA, into a raw
+// 32 MFMAs per wave. LDS: the halo (6 rows x 40 positions of 64 bytes: 32 bf16 channels)
+// and kWideSlots tap slots of 256 rows x 64 bytes. Both are read 16 rows x 4 16-byte groups
+// per fragment, and both keep group s of row (or halo position) r in 16-byte slot
+// s ^ f(r), f(r) = (r >> 1) & 3. Measured with SQ_LDS_BANK_CONFLICT on gfx950, that pattern
+// reads without bank conflicts at every row offset the kernel uses. An unswizzled
+// 80-byte-row halo, and the slot swizzle ((r >> 1) ^ (r >> 3)) & 3, each cost four conflict
+// cycles per ds_read_b128. A wave's DMA fills 1 KB of a tap slot in lane order (16 rows x
+// 4 slots). With a halo row of 40 positions (a multiple of 8), f of a position depends only
+// on the lane and the tap column, so the A fragment reads take three per-lane bases (one
+// per tap column) plus immediate offsets. The next chunk's halo also arrives by LDS DMA, into a raw
 // staging area, and is transposed LDS to LDS at the chunk boundary. So every vector memory
 // operation in the main loop is a DMA at a fixed place in program order, and the vmcnt waits
 // below, which count them, hold whatever the compiler does with other loads. (Counting
@@ -463,7 +468,9 @@ constexpr int kWideSlot = TileW::BN * 64;      // bytes per tap slot
 // of each (channel, halo row), padded to one 256-lane block.
 constexpr int kRawA = 12 * 1024;
 constexpr int kRawB = 1024;
-constexpr int kWideLds = kWideSlots * kWideSlot + TileW::HPOS * kRow + kRawA + kRawB;
+constexpr int kWHP = 40;                                    // halo positions per row (>= 34, multiple of 8)
+constexpr int kWideHalo = TileW::HR * kWHP * 64;            // 6 rows x 40 positions x 64 bytes
+constexpr int kWideLds = kWideSlots * kWideSlot + kWideHalo + kRawA + kRawB;
 static_assert(TileW::HR == 6 && TileW::HC == 34 && Elem<true>::CK == 32, "raw halo staging covers 32 x 6 x 34");
 static_assert(2 * kWideLds <= 160 * 1024, "two wide workgroups per CU");
 
@@ -478,7 +485,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void c
     __shared__ __attribute__((aligned(1024))) unsigned char smem[kWideLds];
     unsigned char* ring = smem;
     unsigned char* halo = smem + kWideSlots * kWideSlot;
-    unsigned char* raw = halo + TL::HPOS * kRow;
+    unsigned char* raw = halo + kWideHalo;
 
     int bid = xcd_contiguous_index(blockIdx.x, gridDim.x);
     const int ot = bid % ocTiles; bid /= ocTiles;
@@ -511,7 +518,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void c
     // 16 rows, 4 per wave. Lane l covers row l >> 2 of its block, physical slot l & 3, which
     // holds K group (l & 3) ^ f(l >> 2).
     const int dma_r = lane >> 2;
-    const int dma_grp = (lane & 3) ^ (((dma_r >> 1) ^ (dma_r >> 3)) & 3);
+    const int dma_grp = (lane & 3) ^ ((dma_r >> 1) & 3);
     auto issue = [&](int s) {
         const int slot = s % kWideSlots;
         const int rowbase = s * CoutPad + oc0;  // [chunk][tap] row index: (chunk * 9 + tap) * CoutPad
@@ -525,8 +532,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void c
         }
     };
     // fragment offsets: A from the halo as in the narrow bf16 kernel, B from a tap slot
-    const unsigned char* a_base = halo + (row0 * TL::HP + i) * kRow + g * 16;
-    const int b_off = (woi * TL::WOB * 16 + i) * 64 + 16 * (g ^ (((i >> 1) ^ (i >> 3)) & 3));
+    // A: halo position p = (row0 + row) * kWHP + block * 16 + i + kw keeps its group g in slot
+    // g ^ ((p >> 1) & 3) = g ^ (((i + kw) >> 1) & 3), since every other term of p is a
+    // multiple of 8: one base per tap column kw
+    const unsigned char* a_base[3];
+#pragma unroll
+    for (int kw = 0; kw < 3; ++kw)
+        a_base[kw] = halo + (row0 * kWHP + i + kw) * 64 + 16 * (g ^ (((i + kw) >> 1) & 3));
+    const int b_off = (woi * TL::WOB * 16 + i) * 64 + 16 * (g ^ ((i >> 1) & 3));
 
     // Halo DMA of the chunk starting at channel c0 into the raw staging area: 12 instructions
     // of 16-byte runs and 4 of 4-byte runs, 4 per wave (3 + 1). Raw 16-byte entry
@@ -554,26 +567,37 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void c
             __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (lds_t*)(raw + kRawA + wave * 256), 4, off, 0, 0, 0);
         }
     };
-    // Raw staging -> channel-minor halo rows (the layout the A fragments read): item
-    // (channel group q, column group cg, halo row r) gathers its 8 channels' runs and
-    // writes them transposed, as the register-staged narrow kernel does.
+    // Raw staging -> channel-minor halo positions (the layout the A fragments read): item
+    // (channel group q, column group cg, halo row r) gathers its 8 channels' runs and writes
+    // pixel p of them as one 16-byte group (a byte permute per output dword) to halo position
+    // r * kWHP + 8 cg + p, slot q ^ f(position). Columns 34-39 receive zeros.
     auto halo_transpose = [&]() {
-        HaloVec<true, TL> hv;
         int q, cg, r;
         HaloVec<true, TL>::item(tid, q, cg, r);
         if (tid < HaloVec<true, TL>::ITEMS) {
+            u4 v[8];
             if (cg < 4) {
 #pragma unroll
-                for (int e = 0; e < 8; ++e) hv.v[0][e] = *(const u4*)(raw + (e * 96 + (r * 4 + cg) * 4 + q) * 16);
+                for (int e = 0; e < 8; ++e) v[e] = *(const u4*)(raw + (e * 96 + (r * 4 + cg) * 4 + q) * 16);
             } else {
 #pragma unroll
                 for (int e = 0; e < 8; ++e)
-                    hv.v[0][e] = u4{*(const unsigned*)(raw + kRawA + (e * 24 + r * 4 + q) * 4), 0u, 0u, 0u};
+                    v[e] = u4{*(const unsigned*)(raw + kRawA + (e * 24 + r * 4 + q) * 4), 0u, 0u, 0u};
             }
-            hv.store(halo, tid);
+#pragma unroll
+            for (int p = 0; p < 8; ++p) {
+                const int dw = p >> 1;
+                const unsigned sel = (p & 1) ? 0x07060302u : 0x05040100u;
+                u4 o;
+#pragma unroll
+                for (int k = 0; k < 4; ++k) o[k] = __builtin_amdgcn_perm(v[2 * k + 1][dw], v[2 * k][dw], sel);
+                const int pos = r * kWHP + cg * 8 + p;
+                *(u4*)(halo + pos * 64 + 16 * (q ^ ((pos >> 1) & 3))) = o;
+            }
         }
     };
-    static_assert(HaloVec<true, TL>::PER == 1 && HaloVec<true, TL>::NCG == 5, "one transpose item per thread");
+    static_assert(HaloVec<true, TL>::PER == 1 && HaloVec<true, TL>::NCG == 5 && 8 * 5 == kWHP,
+                  "one transpose item per thread; five 8-pixel column groups fill a halo row");
 
     const int nsteps = nChunk * 9;
     halo_issue(0);
@@ -608,7 +632,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void c
             u4 a[TL::WPB], b[TL::WOB];
 #pragma unroll
             for (int j = 0; j < TL::WPB; ++j)
-                a[j] = *(const u4*)(a_base + ((j / TL::CB + kh) * TL::HP + (j % TL::CB) * 16 + kw) * kRow);
+                a[j] = *(const u4*)(a_base[kw] + ((j / TL::CB + kh) * kWHP + (j % TL::CB) * 16) * 64);
 #pragma unroll
             for (int j = 0; j < TL::WOB; ++j) b[j] = *(const u4*)(bslot + j * 16 * 64);
 #pragma unroll
