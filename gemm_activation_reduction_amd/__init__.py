@@ -174,6 +174,30 @@ def flse_mish_rows(y, M, N, scale, cmin, cmax, out, stream=None) -> None:
                                          _ptr(out), _stream(stream)))
 
 
+def _device_of(*tensors) -> torch.device:
+    """The one device every tensor sits on (ValueError if they differ)."""
+    dev = tensors[0].device
+    for t in tensors[1:]:
+        if t.device != dev:
+            raise ValueError(f"all tensors must be on one device (found {dev} and {t.device})")
+    return dev
+
+
+def _prepare_out(out, shape, device) -> torch.Tensor:
+    """A new float32 output of `shape` on `device`, or the caller's `out` once it is checked
+    to be a contiguous float32 tensor on `device` with exactly that many elements (any
+    shape: the kernels write the elements in that order, every one and nothing beyond)."""
+    shape = tuple(int(d) for d in shape)
+    if out is None:
+        return torch.empty(shape, dtype=torch.float32, device=device)
+    want = 1
+    for d in shape:
+        want *= d
+    if out.dtype != torch.float32 or out.device != device or not out.is_contiguous() or out.numel() != want:
+        raise ValueError(f"out must be a contiguous float32 tensor of {want} elements (shape {shape}) on {device}")
+    return out
+
+
 def _act_code(act) -> int:
     return _ACT_NAMES[act] if isinstance(act, str) else int(act)
 
@@ -192,11 +216,11 @@ def conv_act_pool(x: torch.Tensor, w: torch.Tensor, b: torch.Tensor, act="gelu",
     Cout = w.shape[0]
     if tuple(w.shape) != (Cout, Cin, 3, 3) or tuple(b.shape) != (Cout,):
         raise ValueError("w must be (Cout, Cin, 3, 3) and b (Cout,)")
-    shape = (N, Cout) if pool else (N, Cout, H - 2, W - 2)
-    if out is None:
-        out = torch.empty(shape, dtype=torch.float32, device=x.device)
+    dev = _device_of(x, w, b)
+    out = _prepare_out(out, (N, Cout) if pool else (N, Cout, H - 2, W - 2), dev)
     code = _act_code(act) | (DT_BF16 if x.dtype == torch.bfloat16 else DT_F32)
-    fconv_act_pool(x, w, b, N, Cin, H, W, Cout, code, 1 if pool else 0, out, stream)
+    with torch.cuda.device(dev):
+        fconv_act_pool(x, w, b, N, Cin, H, W, Cout, code, 1 if pool else 0, out, stream)
     return out
 
 
@@ -215,11 +239,11 @@ def conv2d_act_pool(x: torch.Tensor, w: torch.Tensor, b: torch.Tensor, stride: i
     if tuple(w.shape) != (Cout, Cin, K, K) or tuple(b.shape) != (Cout,):
         raise ValueError("w must be (Cout, Cin, K, K) and b (Cout,)")
     OH, OW = (H + 2 * pad - K) // stride + 1, (W + 2 * pad - K) // stride + 1
-    shape = (N, Cout) if pool else (N, Cout, OH, OW)
-    if out is None:
-        out = torch.empty(shape, dtype=torch.float32, device=x.device)
+    dev = _device_of(x, w, b)
+    out = _prepare_out(out, (N, Cout) if pool else (N, Cout, max(OH, 0), max(OW, 0)), dev)
     code = _act_code(act) | (DT_BF16 if x.dtype == torch.bfloat16 else DT_F32)
-    fconv2d_act_pool(x, w, b, N, Cin, H, W, Cout, K, stride, pad, code, 1 if pool else 0, out, stream)
+    with torch.cuda.device(dev):
+        fconv2d_act_pool(x, w, b, N, Cin, H, W, Cout, K, stride, pad, code, 1 if pool else 0, out, stream)
     return out
 
 
@@ -237,10 +261,11 @@ def gemm_lse_mish(x: torch.Tensor, w: torch.Tensor, b: torch.Tensor, scale: floa
     N = w.shape[0]
     if tuple(w.shape) != (N, K) or tuple(b.shape) != (N,):
         raise ValueError("w must be (N, K) and b (N,)")
-    if out is None:
-        out = torch.empty((M, 1), dtype=torch.float32, device=x.device)
+    dev = _device_of(x, w, b)
+    out = _prepare_out(out, (M, 1), dev)
     call = fgemm_lse_mish_bf16 if x.dtype == torch.bfloat16 else fgemm_lse_mish
-    call(x, w, b, M, K, N, scale, cmin, cmax, out, stream)
+    with torch.cuda.device(dev):
+        call(x, w, b, M, K, N, scale, cmin, cmax, out, stream)
     return out
 
 
@@ -249,9 +274,9 @@ def act_pool(x: torch.Tensor, act="gelu", out: torch.Tensor | None = None, strea
     if x.dtype != torch.float32 or not x.is_cuda or not x.is_contiguous():
         raise ValueError("x must be a contiguous float32 device tensor")
     N, C, H, W = x.shape
-    if out is None:
-        out = torch.empty((N, C), dtype=torch.float32, device=x.device)
-    fact_pool(x, N, C, H, W, _act_code(act), out, stream)
+    out = _prepare_out(out, (N, C), x.device)
+    with torch.cuda.device(x.device):
+        fact_pool(x, N, C, H, W, _act_code(act), out, stream)
     return out
 
 
@@ -259,9 +284,9 @@ def act_elementwise(x: torch.Tensor, act="mish2", out: torch.Tensor | None = Non
     """Tensor helper: float32 x -> act(x) (out may be x itself)."""
     if x.dtype != torch.float32 or not x.is_cuda or not x.is_contiguous():
         raise ValueError("x must be a contiguous float32 device tensor")
-    if out is None:
-        out = torch.empty_like(x)
-    fact_elementwise(x, x.numel(), _act_code(act), out, stream)
+    out = _prepare_out(out, x.shape, x.device)
+    with torch.cuda.device(x.device):
+        fact_elementwise(x, x.numel(), _act_code(act), out, stream)
     return out
 
 
@@ -271,9 +296,9 @@ def lse_mish_rows(y: torch.Tensor, scale: float = 4.0, cmin: float = -10.0, cmax
     if y.dtype != torch.float32 or not y.is_cuda or not y.is_contiguous() or y.dim() != 2:
         raise ValueError("y must be a contiguous 2-D float32 device tensor")
     M, N = y.shape
-    if out is None:
-        out = torch.empty((M, 1), dtype=torch.float32, device=y.device)
-    flse_mish_rows(y, M, N, scale, cmin, cmax, out, stream)
+    out = _prepare_out(out, (M, 1), y.device)
+    with torch.cuda.device(y.device):
+        flse_mish_rows(y, M, N, scale, cmin, cmax, out, stream)
     return out
 
 

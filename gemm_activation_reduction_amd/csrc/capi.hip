@@ -1,5 +1,6 @@
 // C ABI of the fused conv / GEMM-logsumexp library: argument validation, the
 // per-(device, stream) workspace cache, and dispatch to the kernels.
+#include <atomic>
 #include <cmath>
 #include <cstdint>
 #include <cstdio>
@@ -76,9 +77,11 @@ struct EventTimer final : fconv::KernelTimer {
         hipEvent_t start, stop;
     };
     std::mutex mu;
-    bool enabled = false;
+    std::atomic<bool> enabled{false};
     std::vector<Pending> pending;
-    std::map<std::string, hipEvent_t> open;
+    // start events of the kernels in flight, per (kernel, stream): calls on several
+    // streams may be timed at once
+    std::map<std::pair<std::string, hipStream_t>, hipEvent_t> open;
     std::map<std::string, std::pair<double, long long>> totals;  // ms, launches
 
     void begin(const char* kernel, hipStream_t s) override {
@@ -86,19 +89,21 @@ struct EventTimer final : fconv::KernelTimer {
         if (hipEventCreate(&e) != hipSuccess) return;
         (void)hipEventRecord(e, s);
         std::lock_guard<std::mutex> lock(mu);
-        open[kernel] = e;
+        hipEvent_t& slot = open[std::make_pair(std::string(kernel), s)];
+        if (slot) (void)hipEventDestroy(slot);  // a begin without its end: drop the stale start
+        slot = e;
     }
     void end(const char* kernel, hipStream_t s) override {
         hipEvent_t e;
         if (hipEventCreate(&e) != hipSuccess) return;
         (void)hipEventRecord(e, s);
         std::lock_guard<std::mutex> lock(mu);
-        auto it = open.find(kernel);
+        auto it = open.find(std::make_pair(std::string(kernel), s));
         if (it == open.end()) {
             (void)hipEventDestroy(e);
             return;
         }
-        pending.push_back({kernel, it->second, e});
+        pending.push_back({std::string(kernel), it->second, e});
         open.erase(it);
     }
     // Waits for recorded events and folds them into the totals.
@@ -122,7 +127,7 @@ struct EventTimer final : fconv::KernelTimer {
 
 EventTimer g_timer;
 
-fconv::KernelTimer* active_timer() { return g_timer.enabled ? &g_timer : nullptr; }
+fconv::KernelTimer* active_timer() { return g_timer.enabled.load() ? &g_timer : nullptr; }
 
 // Brackets a single-kernel entry point with the timer (when profiling is on).
 struct ActivePlanTimer {

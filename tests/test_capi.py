@@ -177,3 +177,40 @@ def test_epilogue_validation(call, frag):
         call()
     assert e.value.code == fc.FCONV_EINVAL
     assert frag in e.value.message
+
+
+def test_tensor_helpers_check_a_caller_supplied_out():
+    """The tensor helpers pass `out` to kernels that write a fixed number of elements: a
+    caller's buffer of another size, dtype or layout is rejected before any launch."""
+    import torch
+    cpu = torch.device("cpu")
+    assert fc._prepare_out(None, (2, 3), cpu).shape == (2, 3)
+    ok = torch.empty(6)
+    assert fc._prepare_out(ok, (2, 3), cpu) is ok           # any shape with the right element count
+    assert fc._prepare_out(torch.empty(4, 1), (4,), cpu) is not None
+    for bad in (torch.empty(5), torch.empty(7), torch.empty(6, dtype=torch.float64),
+                torch.empty(3, 4)[:, :2], torch.empty(6, device="meta")):
+        with pytest.raises(ValueError, match="out must be"):
+            fc._prepare_out(bad, (2, 3), cpu)
+
+
+def test_tensor_helpers_need_one_device():
+    import torch
+    a, m = torch.empty(1), torch.empty(1, device="meta")
+    assert fc._device_of(a, a, a) == a.device
+    with pytest.raises(ValueError, match="one device"):
+        fc._device_of(a, m)
+
+
+@pytest.mark.gpu
+def test_conv_helper_rejects_a_short_out_before_launch():
+    import torch
+    x = torch.zeros((1, 4, 8, 8), device="cuda")
+    w = torch.zeros((8, 4, 3, 3), device="cuda")
+    b = torch.zeros(8, device="cuda")
+    short = torch.empty((1, 8, 6, 5), device="cuda")        # one column short of (1, 8, 6, 6)
+    with pytest.raises(ValueError, match="out must be"):
+        fc.conv_act_pool(x, w, b, act="gelu", pool=False, out=short)
+    with pytest.raises(ValueError, match="out must be"):
+        fc.gemm_lse_mish(torch.zeros((4, 8), device="cuda"), torch.zeros((3, 8), device="cuda"),
+                         torch.zeros(3, device="cuda"), out=torch.empty(3, device="cuda"))
