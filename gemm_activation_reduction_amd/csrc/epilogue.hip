@@ -58,7 +58,7 @@ __global__ __launch_bounds__(kThreads) void act_pool_map(const float* __restrict
     if (threadIdx.x == 0) out[blockIdx.x] = s * inv_count;
 }
 
-// out[i] = act(x[i]); out may be x. Grid-stride over 16-byte groups, then the tail.
+// out[i] = act(x[i]); out may be x. Workgroups stream 16 KB chunks of 16-byte groups, then the tail.
 template <int ACT, bool VEC>
 __global__ __launch_bounds__(kThreads) void act_elementwise(const float* x, float* out, long long count) {
     const long long stride = (long long)gridDim.x * kThreads;
