@@ -354,6 +354,40 @@ def test_lse_shift_equivariance_and_column_permutation():
     np.testing.assert_allclose(z4, z + 800.0, rtol=1e-14)
 
 
+def _mish_rational(v):
+    """mish(v) = v (e^2v + 2e^v) / (e^2v + 2e^v + 2): tanh(log(1 + t)) = ((1+t)^2 - 1) / ((1+t)^2 + 1),
+    t = e^v -- an algebraic form with no tanh or softplus in it."""
+    t = np.exp(v)
+    q = t * t + 2.0 * t
+    return v * q / (q + 2.0)
+
+
+def test_lse_mish_rows_matches_scipy_and_closed_forms():
+    # random rows: z against SciPy's logsumexp, out against z * mish(z) in the rational form
+    r = np.random.default_rng(31)
+    c = r.uniform(-10.0, 10.0, (5, 613))
+    out, z = oracle.lse_mish_rows(c)
+    rz = scipy.special.logsumexp(c, axis=1)
+    np.testing.assert_allclose(z, rz, rtol=1e-14, atol=1e-14)
+    np.testing.assert_allclose(out, rz * _mish_rational(rz), rtol=1e-13)
+    # a constant row c gives z = c + ln N exactly (every shifted term is e^0 = 1)
+    for cval, N in ((-10.0, 6144), (0.0, 1), (2.5, 7), (10.0, 8192)):
+        out, z = oracle.lse_mish_rows(np.full((2, N), cval))
+        zz = cval + math.log(N)
+        np.testing.assert_allclose(z, zz, rtol=1e-15, atol=1e-15)
+        np.testing.assert_allclose(out, zz * _mish_rational(zz), rtol=1e-13, atol=1e-15)
+    # the l2_p22 page's worked example: every value clamped at 10 over 8192 columns
+    g = json.load(open(os.path.join(GOLDEN, "lse_all_clamped.json")))
+    out, z = oracle.lse_mish_rows(np.full((1, g["N"]), g["clamp_value"]))
+    assert abs(z[0] - g["lse_approx"]) < g["lse_approx_tol"]
+    assert abs(out[0] - g["out_approx"]) < g["out_approx_tol"]
+    # one dominant entry: z lies in [max, max + ln N] and tends to the max
+    row = np.full((1, 100), -50.0)
+    row[0, 37] = 3.0
+    _, z = oracle.lse_mish_rows(row)
+    assert 3.0 <= z[0] <= 3.0 + 99 * math.exp(-53.0) + 1e-15
+
+
 def test_lse_pages_worked_magnitude_example():
     g = json.load(open(os.path.join(GOLDEN, "lse_all_clamped.json")))
     N, v = g["N"], g["clamp_value"]
