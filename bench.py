@@ -1,15 +1,24 @@
 """Benchmark of the fused conv / GEMM-logsumexp library on one MI355X.
 
-    python bench.py [--steps K] [--warmup W] [--workload NAME] [--cpu-seconds S] [--cold-steps C]
+    python bench.py [--steps K] [--warmup W] [--workload NAME|baseline] [--cpu-seconds S]
+                    [--cpu-seconds-each S] [--cold-steps C]
 
 A step is one call of the fused operation (all of its kernels) on one batch of
-synthetic input already resident in HBM. The default workload is the fp32
-conv3x3 + bias + erf-GELU + global average pool on x (64, 16, 224, 224) ->
-(64, 64). Prints ONE JSON line with the whole-job throughput (TFLOP/s of the
-algorithmic contraction), the roofline of the dominant kernel (its average
-launch time from HIP events recorded on the launch stream during the timed
-steps) and a CPU baseline: the fp64 oracle timed on this host on a bounded
-sample of the same workload.
+synthetic input already resident in HBM. Prints ONE JSON line.
+
+The default (--workload baseline) measures the five baseline configurations in one
+process. The line's top-level fields are the headline: the fp32 conv3x3 + bias +
+erf-GELU + global average pool on x (64, 16, 224, 224) -> (64, 64). Its "configs"
+object holds the same figures for the other four: the tiny conv (2, 3, 16, 16) -> (2, 8),
+the fp32 conv + Mish∘Mish with the full (32, 128, 190, 190) output, the bf16 conv +
+GELU + pool on (16, 128, 128, 128) -> (16, 256), and the fp32 GEMM (2048 x 4096 x 6144)
++ scale + clamp + row logsumexp + z*mish(z). Each carries the whole-step throughput
+(TFLOP/s of the algorithmic contraction), the roofline of its dominant kernel (average
+launch time from HIP events recorded on the launch stream during timed steps) against
+the spec peak and against the sustained MFMA rate measured on this part at the start of
+the run, and a CPU baseline: the fp64 oracle timed on this host's cores on a bounded
+sample of the same workload, with the GPU-over-oracle speed-up. --workload NAME measures
+one workload only (the form the profiler runs use).
 """
 from __future__ import annotations
 
@@ -30,7 +39,10 @@ import synth  # noqa: E402
 
 PEAK_TFLOPS = {"f32": 157.3, "bf16": 2516.6}  # MI355X dense MFMA peaks
 HBM_GBPS = 8000.0
-DEFAULT_WORKLOAD = "conv_gelu_pool_f32"
+DEFAULT_WORKLOAD = "baseline"
+HEADLINE = "conv_gelu_pool_f32"
+# the other baseline configurations, in their listed order
+BASELINE_OTHERS = ["conv_tiny", "conv_mish2_full_f32", "conv_gelu_pool_bf16", "gemm_lse_mish_f32"]
 _CSRC = "gemm_activation_reduction_amd/csrc/"
 # The sources each measured kernel is compiled from: a traffic summary counts only while
 # they are unchanged since its counters were taken.
@@ -42,6 +54,7 @@ KERNEL_SOURCES = {
     "act_pool_map": [_CSRC + "epilogue.hip", _CSRC + "device_math.h"],
     "act_elementwise": [_CSRC + "epilogue.hip", _CSRC + "device_math.h"],
     "scale_clamp_lse": [_CSRC + "epilogue.hip", _CSRC + "device_math.h"],
+    "mfma_rate_probe": [_CSRC + "probe.hip"],
 }
 
 
@@ -93,6 +106,16 @@ def read_traffic(workload: str, kernel: str):
         return float(vals["hbm_bytes_per_launch"])
     except (KeyError, ValueError):
         return None
+
+
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def oracle_pool_sample(spec, x, w, b, n, oc):
@@ -304,7 +327,9 @@ def bench_epilogue(args, name, spec, torch, fc, dev) -> int:
             done += 1
         el = time.perf_counter() - t0
         cpu = {"value": round(work / el / 1e9, 4), "unit": "GB/s", "cores": oracle.num_threads(), "kind": "oracle",
-               "seconds": round(el, 3), "sample": f"{done} sampled {'maps' if kind == 'pool' else 'batches/rows'}"}
+               "seconds": round(el, 3), "sample": f"{done} sampled {'maps' if kind == 'pool' else 'batches/rows'}",
+               "cpu_model": cpu_model()}
+        cpu["speedup"] = round(value / cpu["value"], 1) if cpu["value"] > 0 else None
     line = {
         "metric": f"epilogue-only {name} GB/s", "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
@@ -322,42 +347,41 @@ def bench_epilogue(args, name, spec, torch, fc, dev) -> int:
     return 0
 
 
-def main() -> int:
-    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    # the shader clock ramps up over the first ~30 back-to-back steps (measured on the 3x3
-    # GELU+pool fp32 workload: 0.64 ms falling to 0.55 ms per step), so the default warm-up
-    # covers the ramp
-    ap.add_argument("--warmup", type=int, default=50)
-    ap.add_argument("--cold-steps", type=int, default=20,
-                    help="steps timed after evicting L2 and the MALL (0: skip)")
-    ap.add_argument("--workload", default=DEFAULT_WORKLOAD,
-                    choices=sorted(list(synth.CONV_WORKLOADS) + list(synth.GEMM_WORKLOADS)
-                                   + list(synth.EPILOGUE_WORKLOADS)))
-    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="oracle time budget (0: skip)")
-    ap.add_argument("--calib-copy-mb", type=int, default=0,
-                    help="after timing, run plain device copies of this size (HBM counter calibration)")
-    args = ap.parse_args()
-    if args.gpus != 1:
-        print(f"bench.py: runs on one GPU only (asked for --gpus {args.gpus}); "
-              "sharding the work over several GPUs is not implemented", file=sys.stderr)
-        return 2
+def measure_sustained_peaks(fc, torch, dev, iters=(2048, 4096)):
+    """Sustained dense MFMA rate (TFLOP/s) of this part for fp32 and bf16: the MFMA-only
+    probe kernel, timed with HIP events on the launch stream (median of 10 launches after 3
+    warm-up launches)."""
+    sink = torch.zeros(1, dtype=torch.float32, device=dev)
+    out = {}
+    for dtype, code, it in (("f32", fc.DT_F32, iters[0]), ("bf16", fc.DT_BF16, iters[1])):
+        for _ in range(3):
+            fc.fconv_mfma_rate_probe(code, it, sink)
+        torch.cuda.synchronize()
+        fc.fconv_profile(True)
+        times = []
+        flops = 0.0
+        for _ in range(10):
+            flops = fc.fconv_mfma_rate_probe(code, it, sink)
+            torch.cuda.synchronize()
+            ms, n = fc.fconv_profile_read("mfma_rate_probe")
+            times.append(ms)
+            fc.fconv_profile(True)
+        fc.fconv_profile(False)
+        med = float(np.median(times))
+        out[dtype] = {"value": round(flops / (med * 1e-3) / 1e12, 1), "unit": "TFLOP/s", "kernel_ms": round(med, 4),
+                      "spec": PEAK_TFLOPS[dtype], "frac_of_spec": round(flops / (med * 1e-3) / 1e12 / PEAK_TFLOPS[dtype], 4)}
+        print(f"bench: sustained {dtype} MFMA rate {out[dtype]['value']} TFLOP/s "
+              f"({100 * out[dtype]['frac_of_spec']:.1f} % of {PEAK_TFLOPS[dtype]})", file=sys.stderr, flush=True)
+    del sink
+    return out
 
-    import torch
-    import gemm_activation_reduction_amd as fc
 
-    dev = torch.device("cuda:0")
-    # Everything runs on a stream of its own (default priority), as a serving loop would:
-    # on torch's default (null) stream every launch also synchronizes with the other
-    # blocking streams, which measured 2-5 % longer per step.
-    torch.cuda.set_stream(torch.cuda.Stream(device=dev))
-    name = args.workload
-    if name in synth.EPILOGUE_WORKLOADS:
-        return bench_epilogue(args, name, synth.EPILOGUE_WORKLOADS[name], torch, fc, dev)
+def prepare(name, torch, fc, dev):
+    """Inputs resident on the device and a step closure for one conv or GEMM workload."""
     is_conv = name in synth.CONV_WORKLOADS
     spec = synth.CONV_WORKLOADS[name] if is_conv else synth.GEMM_WORKLOADS[name]
     print(f"bench: generating inputs for {name}", file=sys.stderr, flush=True)
+    w_ = {"name": name, "spec": spec, "is_conv": is_conv}
     if is_conv:
         x, w, b = synth.conv_inputs(spec)
         bf16 = spec["dtype"] == "bf16"
@@ -373,11 +397,13 @@ def main() -> int:
         def step():
             fc.conv2d_act_pool(xd, wd, bd, stride=S, pad=P, act=act, pool=bool(spec["pool"]), out=out)
         # the 3x3 path runs the wide kernel for bf16 with Cout >= 256 (the library's timer
-        # names whichever ran; see below)
-        kernel = "conv3x3_fused" if (K, S, P) == (3, 1, 0) else "conv_general_fused"
-        flops, nbytes, dtype = conv_flops(spec), conv_bytes(spec), spec["dtype"]
-        cfg = {"workload": name, "x": [spec["N"], spec["Cin"], spec["H"], spec["W"]], "cout": spec["Cout"],
-               "kernel": f"{K}x{K} stride {S} pad {P}", "act": act, "pool": bool(spec["pool"]), "dtype": dtype}
+        # names whichever ran)
+        kernels = ["conv3x3_fused", "conv3x3_wide_bf16"] if (K, S, P) == (3, 1, 0) else ["conv_general_fused"]
+        w_.update(host=(x, w, b), step=step, out=out, flops=conv_flops(spec), nbytes=conv_bytes(spec),
+                  kernels=kernels, dtype=spec["dtype"],
+                  cfg={"workload": name, "x": [spec["N"], spec["Cin"], spec["H"], spec["W"]], "cout": spec["Cout"],
+                       "kernel": f"{K}x{K} stride {S} pad {P}", "act": act, "pool": bool(spec["pool"]),
+                       "dtype": spec["dtype"]})
     else:
         X, W, b = synth.gemm_inputs(spec)
         dtype = spec.get("dtype", "f32")
@@ -388,11 +414,17 @@ def main() -> int:
 
         def step():
             fc.gemm_lse_mish(xd, wd, bd, spec["scale"], spec["cmin"], spec["cmax"], out=out)
-        flops, nbytes, kernel = gemm_flops(spec), gemm_bytes(spec), "gemm_lse_partials"
-        cfg = {"workload": name, "M": spec["M"], "K": spec["K"], "N": spec["N"], "scale": spec["scale"],
-               "clamp": [spec["cmin"], spec["cmax"]], "dtype": dtype}
+        w_.update(host=(X, W, b), step=step, out=out, flops=gemm_flops(spec), nbytes=gemm_bytes(spec),
+                  kernels=["gemm_lse_partials"], dtype=dtype,
+                  cfg={"workload": name, "M": spec["M"], "K": spec["K"], "N": spec["N"], "scale": spec["scale"],
+                       "clamp": [spec["cmin"], spec["cmax"]], "dtype": dtype})
+    return w_
 
-    print(f"bench: warmup {args.warmup}, timing {args.steps} steps", file=sys.stderr, flush=True)
+
+def time_workload(wl, args, torch, fc, dev, sustained):
+    """Warm-up, whole-step timing, per-kernel event timing, warm/cold medians."""
+    step, flops, nbytes, dtype = wl["step"], wl["flops"], wl["nbytes"], wl["dtype"]
+    print(f"bench: {wl['name']}: warmup {args.warmup}, timing {args.steps} steps", file=sys.stderr, flush=True)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -412,10 +444,12 @@ def main() -> int:
     for _ in range(args.steps):
         step()
     torch.cuda.synchronize()
-    kms, klaunches = fc.fconv_profile_read(kernel)
-    if klaunches == 0 and kernel == "conv3x3_fused":
-        kernel = "conv3x3_wide_bf16"
-        kms, klaunches = fc.fconv_profile_read(kernel)
+    kernel, kms, klaunches = wl["kernels"][0], 0.0, 0
+    for k in wl["kernels"]:
+        kms, klaunches = fc.fconv_profile_read(k)
+        if klaunches:
+            kernel = k
+            break
     others = {k: fc.fconv_profile_read(k) for k in ("pack_weights", "pool_finalize", "lse_merge_mish")}
     fc.fconv_profile(False)
     # timed regions 3 and 4: per-step events with warm caches (median), then cold caches
@@ -426,52 +460,130 @@ def main() -> int:
     value = flops / (ms_per_step * 1e-3) / 1e12
     achieved = flops / (kernel_ms * 1e-3) / 1e12
     peak = PEAK_TFLOPS[dtype]
-    traffic = read_traffic(name, kernel)
+    sus = sustained.get(dtype, {}).get("value") if sustained else None
     for k, (ms, nl) in others.items():
         if nl:
-            print(f"bench: {k} {ms / nl * 1e3:.2f} us/launch", file=sys.stderr, flush=True)
-    print(f"bench: {ms_per_step:.4f} ms/step (events {ev_ms_per_step:.4f}), {kernel} {kernel_ms:.4f} ms/launch "
-          f"over {klaunches} launches, {achieved:.2f} TFLOP/s, {nbytes / (kernel_ms * 1e-3) / 1e9:.1f} GB/s algorithmic; "
-          f"median step {med_ms:.4f} ms"
+            print(f"bench: {wl['name']}: {k} {ms / nl * 1e3:.2f} us/launch", file=sys.stderr, flush=True)
+    print(f"bench: {wl['name']}: {ms_per_step:.4f} ms/step (events {ev_ms_per_step:.4f}), {kernel} {kernel_ms:.4f} "
+          f"ms/launch over {klaunches} launches, {achieved:.2f} TFLOP/s ({100 * achieved / peak:.1f} % of spec"
+          + (f", {100 * achieved / sus:.1f} % of sustained" if sus else "") + "), "
+          f"{nbytes / (kernel_ms * 1e-3) / 1e9:.1f} GB/s algorithmic; median step {med_ms:.4f} ms"
           + (f", cold-cache median {cold_ms:.4f} ms ({flops / (cold_ms * 1e-3) / 1e12:.2f} TFLOP/s)" if ncold else ""),
           file=sys.stderr, flush=True)
-
-    calibration_copies(args, torch, dev)
-
-    cpu = None
-    if args.cpu_seconds > 0:
-        print(f"bench: CPU oracle baseline (~{args.cpu_seconds:.0f} s)", file=sys.stderr, flush=True)
-        if is_conv and spec["pool"]:
-            cpu = cpu_baseline_conv(spec, x, w, b, out.cpu().numpy(), args.cpu_seconds)
-        elif is_conv:
-            cpu = cpu_baseline_conv_points(spec, x, w, b, out, args.cpu_seconds)
-        else:
-            cpu = cpu_baseline_gemm(spec, X, W, b, out.cpu().numpy()[:, 0], args.cpu_seconds)
-
-    line = {
-        "metric": "fused conv+act+pool TFLOP/s and % MFMA peak; GEMM-LSE TFLOP/s",
-        "value": round(value, 3),
-        "unit": "TFLOP/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 5),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": dtype,
-        "data": "synthetic",
-        "config": cfg,
+    return {
+        "value": round(value, 3), "unit": "TFLOP/s", "ms_per_step": round(ms_per_step, 5), "dtype": dtype,
         "pct_mfma_peak": round(100.0 * value / peak, 2),
         "median_ms_per_step": round(med_ms, 5),
         "cold": {"median_ms_per_step": round(cold_ms, 5), "value": round(flops / (cold_ms * 1e-3) / 1e12, 3),
                  "unit": "TFLOP/s", "steps": ncold, "flush_mib": COLD_FLUSH_MIB} if ncold else None,
         "roofline": {"bound": "mfma", "kernel": kernel, "achieved": round(achieved, 3), "peak": peak,
-                     "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": traffic,
+                     "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
+                     "peak_sustained": sus, "frac_sustained": round(achieved / sus, 4) if sus else None,
+                     "traffic": read_traffic(wl["name"], kernel),
                      "kernel_ms": round(kernel_ms, 5), "algorithmic_bytes": nbytes,
                      "algorithmic_gbps": round(nbytes / (kernel_ms * 1e-3) / 1e9, 1)},
+    }
+
+
+def cpu_baseline(wl, seconds, gpu_value):
+    """The fp64 oracle on a bounded sample of the workload, with the GPU-over-oracle speed-up."""
+    if seconds <= 0:
+        return None
+    print(f"bench: {wl['name']}: CPU oracle baseline (~{seconds:.0f} s)", file=sys.stderr, flush=True)
+    spec, out = wl["spec"], wl["out"]
+    if wl["is_conv"]:
+        x, w, b = wl["host"]
+        if spec["pool"]:
+            cpu = cpu_baseline_conv(spec, x, w, b, out.cpu().numpy(), seconds)
+        else:
+            cpu = cpu_baseline_conv_points(spec, x, w, b, out, seconds)
+    else:
+        X, W, b = wl["host"]
+        cpu = cpu_baseline_gemm(spec, X, W, b, out.cpu().numpy()[:, 0], seconds)
+    cpu["cpu_model"] = cpu_model()
+    cpu["speedup"] = round(gpu_value / cpu["value"], 1) if cpu["value"] > 0 else None
+    return cpu
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    # the shader clock ramps up over the first ~30 back-to-back steps (measured on the 3x3
+    # GELU+pool fp32 workload: 0.64 ms falling to 0.55 ms per step), so the default warm-up
+    # covers the ramp
+    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--cold-steps", type=int, default=20,
+                    help="steps timed after evicting L2 and the MALL (0: skip)")
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD,
+                    choices=["baseline"] + sorted(list(synth.CONV_WORKLOADS) + list(synth.GEMM_WORKLOADS)
+                                                  + list(synth.EPILOGUE_WORKLOADS)))
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="oracle time budget for the headline workload (0: skip every CPU baseline)")
+    ap.add_argument("--cpu-seconds-each", type=float, default=5.0,
+                    help="oracle time budget for each of the other baseline configurations")
+    ap.add_argument("--no-sustained", action="store_true", help="skip the sustained MFMA rate probe")
+    ap.add_argument("--calib-copy-mb", type=int, default=0,
+                    help="after timing, run plain device copies of this size (HBM counter calibration)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: runs on one GPU only (asked for --gpus {args.gpus}); "
+              "sharding the work over several GPUs is not implemented", file=sys.stderr)
+        return 2
+
+    import torch
+    import gemm_activation_reduction_amd as fc
+
+    dev = torch.device("cuda:0")
+    # Everything runs on a stream of its own (default priority), as a serving loop would:
+    # on torch's default (null) stream every launch also synchronizes with the other
+    # blocking streams, which measured 2-5 % longer per step.
+    torch.cuda.set_stream(torch.cuda.Stream(device=dev))
+    name = args.workload
+    if name in synth.EPILOGUE_WORKLOADS:
+        return bench_epilogue(args, name, synth.EPILOGUE_WORKLOADS[name], torch, fc, dev)
+    sustained = None if args.no_sustained else measure_sustained_peaks(fc, torch, dev)
+    head_name = HEADLINE if name == "baseline" else name
+    others = BASELINE_OTHERS if name == "baseline" else []
+
+    wl = prepare(head_name, torch, fc, dev)
+    res = time_workload(wl, args, torch, fc, dev, sustained)
+    calibration_copies(args, torch, dev)
+    cpu = cpu_baseline(wl, args.cpu_seconds, res["value"])
+    line = {
+        "metric": "fused conv+act+pool TFLOP/s and % MFMA peak; GEMM-LSE TFLOP/s",
+        "value": res["value"],
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": res["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": res["dtype"],
+        "data": "synthetic",
+        "config": wl["cfg"],
+        "pct_mfma_peak": res["pct_mfma_peak"],
+        "median_ms_per_step": res["median_ms_per_step"],
+        "cold": res["cold"],
+        "roofline": res["roofline"],
         "cpu_baseline": cpu,
     }
+    del wl
+    if others:
+        configs = {}
+        for other in others:
+            torch.cuda.empty_cache()
+            owl = prepare(other, torch, fc, dev)
+            ores = time_workload(owl, args, torch, fc, dev, sustained)
+            ores["config"] = owl["cfg"]
+            ores["cpu_baseline"] = cpu_baseline(owl, args.cpu_seconds_each if args.cpu_seconds > 0 else 0,
+                                                ores["value"])
+            configs[other] = ores
+            del owl
+        line["configs"] = configs
+    line["sustained_mfma"] = sustained
     print(json.dumps(line), flush=True)
     return 0
 

@@ -31,7 +31,8 @@ _ACT_NAMES = {"none": ACT_NONE, "gelu": ACT_GELU, "mish2": ACT_MISH2, "gelu_tanh
 
 # Symbols the C header declares; the loader checks that every one is exported.
 EXPORTS = ("fconv_act_pool", "fconv2d_act_pool", "fgemm_lse_mish", "fgemm_lse_mish_bf16", "fact_pool", "fact_elementwise", "flse_mish_rows",
-           "fconv_last_error", "fconv_release", "fconv_version", "fconv_profile", "fconv_profile_read")
+           "fconv_last_error", "fconv_release", "fconv_version", "fconv_profile", "fconv_profile_read",
+           "fconv_mfma_rate_probe")
 
 
 class FconvError(RuntimeError):
@@ -78,6 +79,8 @@ def load_library() -> ctypes.CDLL:
     lib.fact_elementwise.restype = ci
     lib.flse_mish_rows.argtypes = [vp, ci, ci, cf, cf, cf, vp, vp]
     lib.flse_mish_rows.restype = ci
+    lib.fconv_mfma_rate_probe.argtypes = [ci, ci, vp, ctypes.POINTER(ctypes.c_double), vp]
+    lib.fconv_mfma_rate_probe.restype = ci
     for name in EXPORTS:
         getattr(lib, name)
     _lib = lib
@@ -127,6 +130,14 @@ def fconv_profile_read(kernel: str) -> tuple[float, int]:
     ms, n = ctypes.c_double(), ctypes.c_longlong()
     _check(load_library().fconv_profile_read(kernel.encode(), ctypes.byref(ms), ctypes.byref(n)))
     return ms.value, n.value
+
+
+def fconv_mfma_rate_probe(dtype, iters, sink, stream=None) -> float:
+    """C ``fconv_mfma_rate_probe``: enqueues the MFMA-only rate probe; returns its FLOP count."""
+    flops = ctypes.c_double()
+    _check(load_library().fconv_mfma_rate_probe(int(dtype), int(iters), _ptr(sink), ctypes.byref(flops),
+                                                _stream(stream)))
+    return flops.value
 
 
 def fconv_act_pool(x, w, b, N, Cin, H, W, Cout, act, pool, out, stream=None) -> None:

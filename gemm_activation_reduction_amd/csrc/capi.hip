@@ -298,6 +298,19 @@ FCONV_API int flse_mish_rows(const float* y, int M, int N, float scale, float cm
     return ok();
 }
 
+FCONV_API int fconv_mfma_rate_probe(int dtype, int iters, float* sink, double* flops, hipStream_t stream) {
+    if (!sink || !flops) return fail(FCONV_EINVAL, "fconv_mfma_rate_probe: null pointer argument");
+    if (dtype != FCONV_DT_F32 && dtype != FCONV_DT_BF16)
+        return fail(FCONV_EINVAL, "fconv_mfma_rate_probe: dtype must be FCONV_DT_F32 or FCONV_DT_BF16");
+    if (iters < 1 || iters > (1 << 20)) return fail(FCONV_EINVAL, "fconv_mfma_rate_probe: iters must be 1 .. 2^20");
+    const bool bf16 = dtype == FCONV_DT_BF16;
+    ActivePlanTimer t(active_timer(), "mfma_rate_probe", stream);
+    hipError_t e = fconv::launch_mfma_probe(bf16, iters, sink, stream);
+    if (e != hipSuccess) return fail(FCONV_EHIP, std::string("fconv_mfma_rate_probe launch: ") + hipGetErrorString(e));
+    *flops = fconv::mfma_probe_flops(bf16, iters);
+    return ok();
+}
+
 FCONV_API int fconv_release(void) {
     std::lock_guard<std::mutex> lock(g_ws_mutex);
     int rc = FCONV_OK;

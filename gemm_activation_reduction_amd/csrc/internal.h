@@ -64,4 +64,9 @@ hipError_t launch_act_elementwise(const float* x, long long count, int act, floa
 hipError_t launch_scale_clamp_lse(const float* y, int M, int N, float scale, float cmin, float cmax, float* out,
                                   hipStream_t stream);
 
+// Sustained matrix-core rate probe (measurement aid): a fixed grid of MFMA-only waves.
+long long mfma_probe_grid();
+double mfma_probe_flops(bool bf16, int iters);
+hipError_t launch_mfma_probe(bool bf16, int iters, float* sink, hipStream_t stream);
+
 }  // namespace fconv

@@ -177,11 +177,29 @@ int fconv_release(void);
  * the summed event time in milliseconds and the number of launches of `kernel` since
  * the last fconv_profile() call. Kernel names: "pack_weights", "conv3x3_fused", "conv3x3_wide_bf16",
  * "conv_general_fused", "pool_finalize", "gemm_lse_partials", "lse_merge_mish", "act_pool_map", "act_elementwise",
- * "scale_clamp_lse". Unknown names read as zero.
+ * "scale_clamp_lse", "mfma_rate_probe". Unknown names read as zero.
  * Returns FCONV_EINVAL for a null argument, FCONV_EHIP if an event wait fails.
  */
 int fconv_profile(int enable);
 int fconv_profile_read(const char* kernel, double* total_ms, long long* launches);
+
+/*
+ * Sustained matrix-core rate probe, for measurement tools (not a fused operation).
+ * Enqueues on `stream` one kernel of a fixed grid whose waves issue only MFMAs
+ * (v_mfma_f32_16x16x4_f32 for dtype FCONV_DT_F32, v_mfma_f32_16x16x32_bf16 for
+ * FCONV_DT_BF16): four independent accumulator chains per wave, `iters` rounds of two
+ * MFMAs per chain, operands alternating between two sets of pseudo-random values. The
+ * clock a part holds under such load is set by its power draw, so the FLOP count divided
+ * by the launch's duration is the dense rate the matrix cores sustain, the ceiling a
+ * contraction kernel can reach on this part (the spec peaks assume 2.4 GHz throughout).
+ *   sink   one float of device memory (never written for finite sums; it keeps the
+ *          compiler from removing the work)
+ *   flops  receives the launch's FLOP count (host pointer)
+ * Timed like the other kernels under fconv_profile, as "mfma_rate_probe".
+ * Returns FCONV_EINVAL for a null pointer, another dtype, or iters outside 1 .. 2^20;
+ * FCONV_EHIP if the launch fails.
+ */
+int fconv_mfma_rate_probe(int dtype, int iters, float* sink, double* flops, hipStream_t stream);
 
 /* Library ABI version (major * 100 + minor). */
 int fconv_version(void);

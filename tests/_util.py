@@ -7,6 +7,9 @@ import synth
 
 TOL_F32 = 1e-4
 TOL_BF16 = 2e-2
+# bf16 inputs: both sides read the same bf16 bytes, products are exact in fp32 and
+# accumulate in fp32, so the fp32 bound also holds (2e-2 stays the acceptance bar)
+TOL_BF16_ARITH = 1e-4
 
 
 def max_rel_err(got, ref) -> float:

@@ -90,3 +90,14 @@ def test_committed_traffic_summaries_are_well_formed():
                       if ":" in line and not line.startswith("#"))
         assert len(fields["source_hash"].strip()) == 16, f
         assert float(fields["hbm_bytes_per_launch"]) > 0, f
+
+
+def test_default_run_covers_every_baseline_configuration():
+    # the default line's headline plus its "configs" object are the five baseline
+    # configurations: the tiny conv, the three full-size convs and the GEMM-LSE
+    assert bench.DEFAULT_WORKLOAD == "baseline"
+    names = [bench.HEADLINE] + bench.BASELINE_OTHERS
+    cfgs = sorted(synth.CONV_WORKLOADS[n]["cfg"] if n in synth.CONV_WORKLOADS else synth.GEMM_WORKLOADS[n]["cfg"]
+                  for n in names)
+    assert cfgs == [1, 2, 3, 4, 5]
+    assert len(set(names)) == 5

@@ -214,3 +214,13 @@ def test_conv_helper_rejects_a_short_out_before_launch():
     with pytest.raises(ValueError, match="out must be"):
         fc.gemm_lse_mish(torch.zeros((4, 8), device="cuda"), torch.zeros((3, 8), device="cuda"),
                          torch.zeros(3, device="cuda"), out=torch.empty(3, device="cuda"))
+
+
+@pytest.mark.parametrize("dtype,iters,sink,frag", [
+    (fc.DT_F32, 16, 0, "null"), (0x200, 16, FAKE, "dtype"), (fc.DT_BF16, 0, FAKE, "iters"),
+    (fc.DT_F32, (1 << 20) + 1, FAKE, "iters"),
+])
+def test_mfma_rate_probe_validation(dtype, iters, sink, frag):
+    with pytest.raises(fc.FconvError) as e:
+        fc.fconv_mfma_rate_probe(dtype, iters, sink, S0)
+    assert e.value.code == fc.FCONV_EINVAL and frag in e.value.message

@@ -1,16 +1,19 @@
 """GPU parity of fconv_act_pool against the fp64 CPU oracle (called through the C ABI).
 
-Small and ragged shapes are compared element by element against the full oracle;
-the full-size workloads (in the launch configuration the benchmark times) are compared
-on sampled outputs the oracle computes one by one. Tolerance: max |g - o| / (1 + |o|)
-<= 1e-4 for fp32 inputs and 2e-2 for bf16 inputs.
+Small and ragged shapes, and every output of the full-size workloads (in the launch
+configuration the benchmark times; the full (32, 128, 190, 190) map one image at a
+time), are compared element by element against the oracle. Tolerance:
+max |g - o| / (1 + |o|) <= 1e-4 for fp32 inputs and 2e-2 for bf16 inputs. The bf16
+cases are also held to 1e-4: both sides read the same bf16 bytes, the products are
+exact in fp32 and accumulate in fp32, so only fp32 summation and epilogue rounding
+separate them, far below 1e-4 at these sizes.
 """
 import numpy as np
 import pytest
 
 import oracle
 import synth
-from tests._util import TOL_BF16, TOL_F32, max_rel_err, to_device, workload_conv_inputs
+from tests._util import TOL_BF16, TOL_BF16_ARITH, TOL_F32, max_rel_err, to_device, workload_conv_inputs
 
 pytestmark = pytest.mark.gpu
 
@@ -53,6 +56,7 @@ def test_conv_small_shapes_full_compare(shape, pool, act, bf16):
     err = max_rel_err(got, ref)
     print(f"shape={shape} pool={pool} act={act} bf16={bf16} err={err:.3e}", flush=True)
     assert err <= (TOL_BF16 if bf16 else TOL_F32)
+    assert err <= TOL_BF16_ARITH
 
 
 def test_conv_tiny_workload():
@@ -110,17 +114,8 @@ def test_conv_deterministic_and_stream():
     assert torch.equal(o1, o2) and torch.equal(o1, o3)
 
 
-def sample_pairs(N, Cout, count, seed):
-    r = np.random.default_rng(seed)
-    n = r.integers(0, N, count)
-    oc = r.integers(0, Cout, count)
-    n[:2], oc[:2] = (0, N - 1), (0, Cout - 1)  # both corners of the (n, oc) grid
-    return n, oc
-
-
-@pytest.mark.parametrize("name,count", [("conv_gelu_pool_f32", 96), ("conv_gelu_pool_bf16", 48),
-                                        ("conv_gelu_tanh_pool_bf16", 32)])
-def test_conv_full_size_pooled_sampled(name, count):
+@pytest.mark.parametrize("name", ["conv_gelu_pool_f32", "conv_gelu_pool_bf16", "conv_gelu_tanh_pool_bf16"])
+def test_conv_full_size_pooled_whole_output(name):
     spec = synth.CONV_WORKLOADS[name]
     bf16 = spec["dtype"] == "bf16"
     x, w, b = workload_conv_inputs(name)
@@ -128,16 +123,16 @@ def test_conv_full_size_pooled_sampled(name, count):
     got = run_conv(x, w, b, spec["act"], 1, bf16)
     assert got.shape == (spec["N"], spec["Cout"])
     assert np.all(np.isfinite(got))
-    n, oc = sample_pairs(spec["N"], spec["Cout"], count, 3)
-    ref = oracle.conv_pool_sample(x, w, b, spec["act"], n, oc)
-    err = max_rel_err(got[n, oc], ref)
-    print(f"{name}: sampled err={err:.3e}", flush=True)
+    ref = oracle.conv_act_pool(x, w, b, spec["act"], 1)
+    err = max_rel_err(got, ref)
+    print(f"{name}: all {got.size} outputs, err={err:.3e}", flush=True)
     assert err <= (TOL_BF16 if bf16 else TOL_F32)
+    assert err <= TOL_BF16_ARITH
 
 
-def test_conv_full_size_mish2_full_output_sampled():
+def test_conv_full_size_mish2_full_output_whole():
+    # every one of the 147.9 M outputs of the (32, 128, 190, 190) map, one image at a time
     name = "conv_mish2_full_f32"
-    spec = synth.CONV_WORKLOADS[name]
     x, w, b = workload_conv_inputs(name)
     xd, wd, bd = to_device(x), to_device(w), to_device(b)
     print(f"{name}: running GPU", flush=True)
@@ -145,32 +140,20 @@ def test_conv_full_size_mish2_full_output_sampled():
     torch.cuda.synchronize()
     N, Cout, OH, OW = out.shape
     assert (N, Cout, OH, OW) == (32, 128, 190, 190)
-    assert bool(torch.isfinite(out).all())
-    r = np.random.default_rng(4)
-    cnt = 20000
-    n, oc = r.integers(0, N, cnt), r.integers(0, Cout, cnt)
-    oh, ow = r.integers(0, OH, cnt), r.integers(0, OW, cnt)
-    # always include the four corners of the first and last maps and a full last row
-    extra = [(0, 0, 0, 0), (0, 0, OH - 1, OW - 1), (N - 1, Cout - 1, 0, OW - 1), (N - 1, Cout - 1, OH - 1, 0)]
-    extra += [(N - 1, Cout - 1, OH - 1, c) for c in range(OW)]
-    n = np.concatenate([n, [e[0] for e in extra]])
-    oc = np.concatenate([oc, [e[1] for e in extra]])
-    oh = np.concatenate([oh, [e[2] for e in extra]])
-    ow = np.concatenate([ow, [e[3] for e in extra]])
-    idx = [torch.from_numpy(a.astype(np.int64)).cuda() for a in (n, oc, oh, ow)]
-    got = out[idx[0], idx[1], idx[2], idx[3]].cpu().numpy()
-    ref = oracle.conv_point_sample(x, w, b, fc.ACT_MISH2, n, oc, oh, ow)
-    err = max_rel_err(got, ref)
-    print(f"{name}: sampled err={err:.3e}", flush=True)
-    assert err <= TOL_F32
+    worst = 0.0
+    for n in range(N):
+        ref = oracle.conv_act_pool(np.ascontiguousarray(x[n:n + 1]), w, b, fc.ACT_MISH2, 0)
+        err = max_rel_err(out[n:n + 1].cpu().numpy(), ref)
+        worst = max(worst, err)
+        assert err <= TOL_F32, (n, err)
+    print(f"{name}: all {out.numel()} outputs, err={worst:.3e}", flush=True)
 
 
 @pytest.mark.parametrize("act", ["none", "gelu"])
 def test_conv_wide_full_map_repeatable_at_workload_size(act):
     # The 16 x 128 x 128^2 -> 256 bf16 inputs with the full (16, 256, 126, 126) map written:
-    # eight launches in a row must agree bit for bit, and sampled outputs (weighted towards
-    # the oc range whose weight rows the last DMA instruction of a K step fills) must match
-    # the oracle. A wait that let a wave pass a barrier before its last DMA had landed made
+    # eight launches in a row must agree bit for bit, and every output must match the
+    # oracle. A wait that let a wave pass a barrier before its last DMA had landed made
     # about half of such launches wrong in one 16-channel block of one wave.
     name = "conv_gelu_pool_bf16"
     spec = synth.CONV_WORKLOADS[name]
@@ -187,16 +170,10 @@ def test_conv_wide_full_map_repeatable_at_workload_size(act):
         fc.conv_act_pool(xd, wd, bd, act=code, pool=False, out=out, stream=s)
         same += int(torch.equal(out, first))
     torch.cuda.synchronize()
-    N, Cout, OH, OW = first.shape
-    r = np.random.default_rng(11)
-    cnt = 6000
-    n, oh, ow = r.integers(0, N, cnt), r.integers(0, OH, cnt), r.integers(0, OW, cnt)
-    oc = np.where(r.random(cnt) < 0.5, r.integers(192, 256, cnt), r.integers(0, Cout, cnt))
-    idx = [torch.from_numpy(a.astype(np.int64)).cuda() for a in (n, oc, oh, ow)]
-    got = first[idx[0], idx[1], idx[2], idx[3]].cpu().numpy()
-    ref = oracle.conv_point_sample(x, w, b, code, n, oc, oh, ow)
-    err = max_rel_err(got, ref)
-    print(f"{name} full map act={act}: {same} of 8 repeats bit-equal, sampled err={err:.3e}", flush=True)
+    ref = oracle.conv_act_pool(x, w, b, code, 0)
+    err = max_rel_err(first.cpu().numpy(), ref)
+    print(f"{name} full map act={act}: {same} of 8 repeats bit-equal, all {first.numel()} outputs "
+          f"err={err:.3e}", flush=True)
     assert same == 8
     assert err <= TOL_F32
 
@@ -210,7 +187,8 @@ def test_conv_pool_repeated_calls_with_changing_shapes():
         x, w, b = rand_case(50 + k % len(cases), *shape, bf16=bf16)
         got = run_conv(x, w, b, fc.ACT_GELU, 1, bf16)
         ref = oracle.conv_act_pool(x, w, b, fc.ACT_GELU, 1)
-        assert max_rel_err(got, ref) <= (TOL_BF16 if bf16 else TOL_F32), (k, shape)
+        err = max_rel_err(got, ref)
+        assert err <= (TOL_BF16 if bf16 else TOL_F32) and err <= TOL_BF16_ARITH, (k, shape, err)
 
 
 def test_conv_image_near_the_32bit_offset_limit():

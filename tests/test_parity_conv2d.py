@@ -10,7 +10,7 @@ import pytest
 
 import oracle
 import synth
-from tests._util import TOL_BF16, TOL_F32, max_rel_err, to_device, workload_conv_inputs
+from tests._util import TOL_BF16, TOL_BF16_ARITH, TOL_F32, max_rel_err, to_device, workload_conv_inputs
 
 pytestmark = pytest.mark.gpu
 
@@ -59,6 +59,7 @@ def test_conv2d_small_shapes_full_compare(geom, shape, pool, bf16):
     err = max_rel_err(got, ref)
     print(f"geom={geom} shape={shape} pool={pool} act={act} bf16={bf16} err={err:.3e}", flush=True)
     assert err <= (TOL_BF16 if bf16 else TOL_F32)
+    assert err <= TOL_BF16_ARITH
 
 
 def test_conv2d_3x3_valid_is_the_fast_path_bit_for_bit():
@@ -85,8 +86,8 @@ def test_conv2d_padding_border_closed_form():
         np.testing.assert_array_equal(got[0, c], expect)
 
 
-@pytest.mark.parametrize("name,count", [("conv5x5_same_gelu_pool_f32", 48), ("conv3x3_s2_gelu_pool_bf16", 48)])
-def test_conv2d_full_size_pooled_sampled(name, count):
+@pytest.mark.parametrize("name", ["conv5x5_same_gelu_pool_f32", "conv3x3_s2_gelu_pool_bf16"])
+def test_conv2d_full_size_pooled_whole_output(name):
     spec = synth.CONV_WORKLOADS[name]
     K, S, P = synth.conv_geometry(spec)
     bf16 = spec["dtype"] == "bf16"
@@ -94,16 +95,15 @@ def test_conv2d_full_size_pooled_sampled(name, count):
     print(f"{name}: running GPU", flush=True)
     got = run_conv2d(x, w, b, S, P, spec["act"], 1, bf16)
     assert got.shape == (spec["N"], spec["Cout"]) and np.all(np.isfinite(got))
-    r = np.random.default_rng(11)
-    n, oc = r.integers(0, spec["N"], count), r.integers(0, spec["Cout"], count)
-    n[:2], oc[:2] = (0, spec["N"] - 1), (0, spec["Cout"] - 1)
-    ref = oracle.conv2d_pool_sample(x, w, b, S, P, spec["act"], n, oc)
-    err = max_rel_err(got[n, oc], ref)
-    print(f"{name}: sampled err={err:.3e}", flush=True)
+    ref = oracle.conv2d_act_pool(x, w, b, S, P, spec["act"], 1)
+    err = max_rel_err(got, ref)
+    print(f"{name}: all {got.size} outputs, err={err:.3e}", flush=True)
     assert err <= (TOL_BF16 if bf16 else TOL_F32)
+    assert err <= TOL_BF16_ARITH
 
 
-def test_conv2d_full_size_1x1_full_output_sampled():
+def test_conv2d_full_size_1x1_full_output_whole():
+    # every output of the (32, 128, 192, 192) map, one image at a time
     name = "conv1x1_mish2_full_f32"
     spec = synth.CONV_WORKLOADS[name]
     K, S, P = synth.conv_geometry(spec)
@@ -114,15 +114,10 @@ def test_conv2d_full_size_1x1_full_output_sampled():
     torch.cuda.synchronize()
     N, Cout, OH, OW = out.shape
     assert (OH, OW) == synth.conv_out_size(spec)
-    assert bool(torch.isfinite(out).all())
-    r = np.random.default_rng(12)
-    cnt = 20000
-    n, oc = r.integers(0, N, cnt), r.integers(0, Cout, cnt)
-    oh, ow = r.integers(0, OH, cnt), r.integers(0, OW, cnt)
-    n[:2], oc[:2], oh[:2], ow[:2] = (0, N - 1), (0, Cout - 1), (0, OH - 1), (0, OW - 1)
-    idx = [torch.from_numpy(a.astype(np.int64)).cuda() for a in (n, oc, oh, ow)]
-    got = out[idx[0], idx[1], idx[2], idx[3]].cpu().numpy()
-    ref = oracle.conv2d_point_sample(x, w, b, S, P, fc.ACT_MISH2, n, oc, oh, ow)
-    err = max_rel_err(got, ref)
-    print(f"{name}: sampled err={err:.3e}", flush=True)
-    assert err <= TOL_F32
+    worst = 0.0
+    for n in range(N):
+        ref = oracle.conv2d_act_pool(np.ascontiguousarray(x[n:n + 1]), w, b, S, P, fc.ACT_MISH2, 0)
+        err = max_rel_err(out[n:n + 1].cpu().numpy(), ref)
+        worst = max(worst, err)
+        assert err <= TOL_F32, (n, err)
+    print(f"{name}: all {out.numel()} outputs, err={worst:.3e}", flush=True)

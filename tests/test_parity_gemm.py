@@ -119,19 +119,17 @@ def test_gemm_deterministic_and_stream():
 
 
 @pytest.mark.parametrize("name", ["gemm_lse_mish_f32", "gemm_lse_mish_bf16"])
-def test_gemm_full_size_sampled_rows(name):
+def test_gemm_full_size_whole_output(name):
     spec = synth.GEMM_WORKLOADS[name]
     X, W, b = workload_gemm_inputs(name)
     print(f"{name}: running GPU", flush=True)
     got = run_gemm(X, W, b, spec["scale"], spec["cmin"], spec["cmax"])
     assert got.shape == (spec["M"],) and np.all(np.isfinite(got))
-    r = np.random.default_rng(6)
-    rows = np.unique(np.concatenate([[0, spec["M"] - 1], r.integers(0, spec["M"], 62)]))
-    ref, z = oracle.gemm_lse_mish(X, W, b, spec["scale"], spec["cmin"], spec["cmax"], rows=rows)
-    err = max_rel_err(got[rows], ref)
-    print(f"{name}: sampled err={err:.3e} z range [{z.min():.3f}, {z.max():.3f}]", flush=True)
+    ref, z = oracle.gemm_lse_mish(X, W, b, spec["scale"], spec["cmin"], spec["cmax"])
+    err = max_rel_err(got, ref)
+    print(f"{name}: all {got.size} rows, err={err:.3e} z range [{z.min():.3f}, {z.max():.3f}]", flush=True)
     assert err <= TOL_F32
-    # LSE bounds hold for every row (property at full size, no oracle needed)
+    # LSE bounds hold for every row
     lo, hi = spec["cmin"] + math.log(spec["N"]), spec["cmax"] + math.log(spec["N"])
     zz_lo, zz_hi = lo * lo * math.tanh(math.log1p(math.exp(lo))), hi * hi
     assert np.all(got >= min(zz_lo, 0.0) - 1e-3) and np.all(got <= zz_hi + 1e-3)
