@@ -30,7 +30,7 @@ DT_F32, DT_BF16 = 0x000, 0x100
 _ACT_NAMES = {"none": ACT_NONE, "gelu": ACT_GELU, "mish2": ACT_MISH2, "gelu_tanh": ACT_GELU_TANH}
 
 # Symbols the C header declares; the loader checks that every one is exported.
-EXPORTS = ("fconv_act_pool", "fconv2d_act_pool", "fgemm_lse_mish", "fgemm_lse_mish_bf16", "fact_pool", "fact_elementwise", "flse_mish_rows",
+EXPORTS = ("fconv_act_pool", "fconv_act_pool_noalloc", "fconv2d_act_pool", "fgemm_lse_mish", "fgemm_lse_mish_bf16", "fact_pool", "fact_elementwise", "flse_mish_rows",
            "fconv_last_error", "fconv_release", "fconv_version", "fconv_profile", "fconv_profile_read",
            "fconv_mfma_rate_probe")
 
@@ -56,6 +56,8 @@ def load_library() -> ctypes.CDLL:
     vp, ci, cf = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
     lib.fconv_act_pool.argtypes = [vp, vp, vp, ci, ci, ci, ci, ci, ci, ci, vp, vp]
     lib.fconv_act_pool.restype = ci
+    lib.fconv_act_pool_noalloc.argtypes = [vp, vp, vp, ci, ci, ci, ci, ci, ci, ci, vp, vp]
+    lib.fconv_act_pool_noalloc.restype = ci
     lib.fconv2d_act_pool.argtypes = [vp, vp, vp, ci, ci, ci, ci, ci, ci, ci, ci, ci, ci, vp, vp]
     lib.fconv2d_act_pool.restype = ci
     lib.fgemm_lse_mish.argtypes = [vp, vp, vp, ci, ci, ci, cf, cf, cf, vp, vp]
@@ -144,6 +146,13 @@ def fconv_act_pool(x, w, b, N, Cin, H, W, Cout, act, pool, out, stream=None) -> 
     """C ``fconv_act_pool``: 3x3 valid conv + bias + activation (+ global mean pool)."""
     rc = load_library().fconv_act_pool(_ptr(x), _ptr(w), _ptr(b), int(N), int(Cin), int(H), int(W), int(Cout),
                                        int(act), int(pool), _ptr(out), _stream(stream))
+    _check(rc)
+
+
+def fconv_act_pool_noalloc(x, w, b, N, Cin, H, W, Cout, act, pool, out, stream=None) -> None:
+    """C ``fconv_act_pool_noalloc``: fconv_act_pool on the library's static scratch (no allocation)."""
+    rc = load_library().fconv_act_pool_noalloc(_ptr(x), _ptr(w), _ptr(b), int(N), int(Cin), int(H), int(W),
+                                               int(Cout), int(act), int(pool), _ptr(out), _stream(stream))
     _check(rc)
 
 

@@ -159,8 +159,38 @@ FCONV_API const char* fconv_last_error(void) { return g_last_error.c_str(); }
 
 namespace {
 
+// Scratch of fconv_act_pool_noalloc: a file-scope device array, so the entry point needs
+// no allocation. Each GPU the library runs on holds its own copy (at its own address) until
+// the process ends. In host code `scratch` names a host-side stand-in; its device address
+// comes from hipGetSymbolAddress, looked up once per device with that device current.
+constexpr size_t kNoAllocScratchBytes = FCONV_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of `scratch` on the current device.
+int noalloc_scratch(void** out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(FCONV_EHIP, std::string("hipGetDevice: ") + hipGetErrorString(e));
+    if (dev < 0 || dev >= kMaxDevices) return fail(FCONV_EUNSUPPORTED, "device index beyond the scratch table");
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p)
+            return fail(FCONV_EHIP, std::string("hipGetSymbolAddress(scratch): ") + hipGetErrorString(e));
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return FCONV_OK;
+}
+
 int conv_impl(const char* name, const void* x, const void* w, const float* b, int N, int Cin, int H, int W,
-              int Cout, int K, int stride, int pad, int act, int pool, float* out, hipStream_t stream) {
+              int Cout, int K, int stride, int pad, int act, int pool, float* out, hipStream_t stream,
+              bool noalloc = false) {
     const std::string fn(name);
     if (!x || !w || !b || !out) return fail(FCONV_EINVAL, fn + ": null pointer argument");
     if (N < 1 || Cin < 1 || Cout < 1) return fail(FCONV_EINVAL, fn + ": N, Cin and Cout must be >= 1");
@@ -194,10 +224,21 @@ int conv_impl(const char* name, const void* x, const void* w, const float* b, in
     if ((long long)Cin * H * W * (long long)esz > 0x7FFF0000LL || (long long)plan.wpack_bytes > 0x7FFF0000LL)
         return fail(FCONV_EUNSUPPORTED, fn + ": one image (or the weights) exceeds 2 GiB");
     void* ws = nullptr;
-    int rc = get_workspace(stream, plan.workspace_bytes(), &ws);
-    if (rc != FCONV_OK) return rc;
-    hipError_t e = fast ? fconv::launch_conv(plan, x, w, b, out, ws, stream, active_timer())
-                        : fconv::launch_conv_general(plan, x, w, b, out, ws, stream, active_timer());
+    if (noalloc) {
+        if (plan.workspace_bytes() > kNoAllocScratchBytes)
+            return fail(FCONV_EINVAL, fn + ": needs " + std::to_string(plan.workspace_bytes()) +
+                                          " bytes of scratch (repacked weights + pool partials); the static scratch "
+                                          "holds " + std::to_string(kNoAllocScratchBytes));
+        int rc = noalloc_scratch(&ws);
+        if (rc != FCONV_OK) return rc;
+    } else {
+        int rc = get_workspace(stream, plan.workspace_bytes(), &ws);
+        if (rc != FCONV_OK) return rc;
+    }
+    // the allocation-free entry point records no timing events either
+    fconv::KernelTimer* timer = noalloc ? nullptr : active_timer();
+    hipError_t e = fast ? fconv::launch_conv(plan, x, w, b, out, ws, stream, timer)
+                        : fconv::launch_conv_general(plan, x, w, b, out, ws, stream, timer);
     if (e != hipSuccess) return fail(FCONV_EHIP, fn + " launch: " + hipGetErrorString(e));
     return ok();
 }
@@ -207,6 +248,11 @@ int conv_impl(const char* name, const void* x, const void* w, const float* b, in
 FCONV_API int fconv_act_pool(const void* x, const void* w, const float* b, int N, int Cin, int H, int W,
                              int Cout, int act, int pool, float* out, hipStream_t stream) {
     return conv_impl("fconv_act_pool", x, w, b, N, Cin, H, W, Cout, 3, 1, 0, act, pool, out, stream);
+}
+
+FCONV_API int fconv_act_pool_noalloc(const void* x, const void* w, const float* b, int N, int Cin, int H, int W,
+                                     int Cout, int act, int pool, float* out, hipStream_t stream) {
+    return conv_impl("fconv_act_pool_noalloc", x, w, b, N, Cin, H, W, Cout, 3, 1, 0, act, pool, out, stream, true);
 }
 
 FCONV_API int fconv2d_act_pool(const void* x, const void* w, const float* b, int N, int Cin, int H, int W,

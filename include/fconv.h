@@ -80,6 +80,27 @@ int fconv_act_pool(const void* x, const void* w, const float* b,
                    int act, int pool, float* out, hipStream_t stream);
 
 /*
+ * fconv_act_pool without any allocation, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc).
+ * Same arguments, results and kernels as fconv_act_pool; the caller still provides x, w,
+ * b and out. Instead of the library's workspace it uses a static device array of
+ * FCONV_NOALLOC_SCRATCH_BYTES (16 MiB) that each GPU the library runs on holds until the
+ * process ends; it needs (repacked weights) + (pool only) N * Cout * tiles * 4 bytes, e.g.
+ * 3.2 MB for x (64, 16, 224, 224) -> 64 pooled. It calls no hipMalloc, hipFree or
+ * allocating library routine, and records no profiling events.
+ * Every call on one GPU shares that GPU's array and leaves its contents behind (every
+ * byte a call reads it has written first, so nothing needs clearing): calls that overlap
+ * on one GPU -- on different streams, or from several host threads -- race and must be
+ * serialized by the caller.
+ * Returns the fconv_act_pool errors, and FCONV_EINVAL (nothing enqueued) when the call
+ * needs more scratch than the array holds.
+ */
+#define FCONV_NOALLOC_SCRATCH_BYTES (16u << 20)
+int fconv_act_pool_noalloc(const void* x, const void* w, const float* b,
+                           int N, int Cin, int H, int W, int Cout,
+                           int act, int pool, float* out, hipStream_t stream);
+
+/*
  * The same fused operation for a K x K kernel with stride and zero padding (nn.Conv2d's
  * kernel_size, stride and padding; the pages fix K = 3, stride 1, padding 0):
  *   pre[n,oc,oh,ow] = b[oc] + sum_{ic, kh<K, kw<K} w[oc,ic,kh,kw] * xp[n, ic, oh*stride + kh - pad,

@@ -224,3 +224,18 @@ def test_mfma_rate_probe_validation(dtype, iters, sink, frag):
     with pytest.raises(fc.FconvError) as e:
         fc.fconv_mfma_rate_probe(dtype, iters, sink, S0)
     assert e.value.code == fc.FCONV_EINVAL and frag in e.value.message
+
+
+def test_noalloc_rejects_a_call_beyond_its_scratch():
+    # pool partials of 512 x 64 x (28 x 7 tiles) x 4 B = 25.7 MB > the 16 MiB static scratch:
+    # EINVAL before any HIP call
+    with pytest.raises(fc.FconvError) as e:
+        fc.fconv_act_pool_noalloc(FAKE, FAKE + (1 << 32), FAKE + (2 << 32), 512, 16, 224, 224, 64,
+                                  fc.ACT_GELU, 1, FAKE + (3 << 32), S0)
+    assert e.value.code == fc.FCONV_EINVAL and "scratch" in e.value.message
+
+
+def test_noalloc_validates_like_the_allocating_entry_point():
+    with pytest.raises(fc.FconvError) as e:
+        fc.fconv_act_pool_noalloc(0, FAKE, FAKE, 2, 3, 16, 16, 8, fc.ACT_GELU, 1, FAKE, S0)
+    assert e.value.code == fc.FCONV_EINVAL and "null" in e.value.message
