@@ -452,6 +452,8 @@ def time_workload(wl, args, torch, fc, dev, sustained):
             break
     others = {k: fc.fconv_profile_read(k) for k in ("pack_weights", "pool_finalize", "lse_merge_mish")}
     fc.fconv_profile(False)
+    if klaunches == 0:
+        raise RuntimeError(f"none of the kernels {wl['kernels']} was timed for {wl['name']}")
     # timed regions 3 and 4: per-step events with warm caches (median), then cold caches
     med_ms, cold_ms, ncold = warm_and_cold(step, args.steps, args.cold_steps, torch, dev)
     ms_per_step = (t1 - t0) * 1e3 / args.steps

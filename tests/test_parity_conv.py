@@ -297,3 +297,31 @@ def test_conv_wide_matches_narrow_full_map(shape):
     o_narrow = fc.conv_act_pool(xu, wd, bd, act="mish2", pool=False)
     torch.cuda.synchronize()
     assert torch.equal(o_wide, o_narrow)
+
+
+# bf16 pooled at the baseline workload's depth (four or more 32-channel chunks) on grids of
+# 1024 or more tiles, four or more per CU: ragged channel chunks, tile rows and columns and
+# oc tiles; tile counts that do not divide evenly among the CUs or the eight XCDs.
+WIDE_DEEP_SHAPES = [
+    (24, 100, 37, 72, 300),   # 1296 tiles: a 4-channel tail chunk, ragged rows, columns and oc tile
+    (75, 128, 30, 40, 256),   # 1050 tiles (not a multiple of 8): exactly four chunks, 7 x 2 tiles per image
+    (33, 160, 66, 64, 256),   # 1056 tiles: five chunks (the fifth without an epilogue slice)
+]
+
+
+@pytest.mark.parametrize("act", [fc.ACT_NONE, fc.ACT_GELU, fc.ACT_MISH2, fc.ACT_GELU_TANH])
+@pytest.mark.parametrize("shape", WIDE_DEEP_SHAPES)
+def test_conv_wide_deep_large_grid_pooled(shape, act):
+    N, Cin, H, W, Cout = shape
+    tiles = N * ((H - 2 + 3) // 4) * ((W - 2 + 31) // 32) * ((Cout + 255) // 256)
+    assert tiles >= 1024 and (Cin + 31) // 32 >= 4
+    x, w, b = rand_case(hash(shape) % 977 + 11, *shape, bf16=True)
+    print(f"wide deep shape={shape} tiles={tiles} act={act}: running GPU", flush=True)
+    got = run_conv(x, w, b, act, 1, True)
+    ref = oracle.conv_act_pool(x, w, b, act, 1)
+    err = max_rel_err(got, ref)
+    print(f"wide deep shape={shape} act={act} err={err:.3e}", flush=True)
+    assert err <= TOL_F32
+    # run to run: bit-equal
+    again = run_conv(x, w, b, act, 1, True)
+    assert np.array_equal(got, again)
