@@ -297,7 +297,7 @@ __global__ __launch_bounds__(TL::NT) void gemm_lse_partials_dma(
     constexpr int BK = TL::BK, ROWS = TL::BM + TL::BN, SB = ROWS * 64;  // bytes per stage
     constexpr int NI = ROWS / 16, NW = TL::NT / 64;                       // DMA instructions per stage, waves
     static_assert(ROWS % 16 == 0 && TL::BM % 16 == 0, "whole 16-row DMA blocks");
-    __shared__ __attribute__((aligned(1024))) unsigned char lds[STAGES * SB];
+    __shared__ __attribute__((aligned(1024))) unsigned char lds[STAGES * SB + 1024];  // + junk DMA target
 
     const int tn = blockIdx.x % tilesN, tm = blockIdx.x / tilesN;
     const int m0 = tm * TL::BM, n0 = tn * TL::BN;
@@ -323,29 +323,39 @@ __global__ __launch_bounds__(TL::NT) void gemm_lse_partials_dma(
     // group (lane & 3) ^ f(lane >> 2).
     const int dma_r = lane >> 2;
     const int dma_grp = (lane & 3) ^ (((dma_r >> 1) ^ (dma_r >> 3)) & 3);
-    auto issue = [&](int buf, int k0) {
+    // Every wave sends exactly IPW DMA instructions per stage, so the per-stage DMA code has no
+    // branches and every wave's vmcnt counts are the same: instruction q of wave w fills
+    // 16-row block w + NW q. The X blocks come first (BM / 16 = 2 NW of them: q = 0, 1, fixed
+    // at compile time), then the W blocks; a block index past the last (wave w + NW q >= NI)
+    // sends an out-of-range load into a junk kilobyte past the ring. K stages are whole
+    // (K is a multiple of 2 BK on this path), so only the row needs a bound.
+    constexpr int IPW = (NI + NW - 1) / NW;
+    static_assert(TL::BM / 16 == 2 * NW && IPW == 4, "X blocks are instructions q = 0, 1; W blocks q = 2, 3");
+    int dma_off[IPW];  // byte offset of this lane's first K group in its row, or kOOB past the operand
 #pragma unroll
-        for (int q = 0; q < (NI + NW - 1) / NW; ++q) {
+    for (int q = 0; q < IPW; ++q) {
+        const int ins = wave + NW * q;
+        const int row = ins * 16 + dma_r;
+        if (q < 2) {
+            const int r = m0 + row;
+            dma_off[q] = r < M ? (r * K + EPG * dma_grp) * ESZ : kOOB;
+        } else {
+            const int r = n0 + row - TL::BM;
+            dma_off[q] = (ins < NI && r < N) ? (r * K + EPG * dma_grp) * ESZ : kOOB;
+        }
+    }
+    auto issue = [&](int buf, int k0) {
+        typedef __attribute__((address_space(3))) void lds_t;
+#pragma unroll
+        for (int q = 0; q < IPW; ++q) {
             const int ins = wave + NW * q;  // wave-uniform
-            if (ins < NI) {
-                const int row = ins * 16 + dma_r;
-                const int k = k0 + EPG * dma_grp;
-                typedef __attribute__((address_space(3))) void lds_t;
-                lds_t* dst = (lds_t*)(lds + buf * SB + ins * 1024);
-                if (ins * 16 < TL::BM) {
-                    const int r = m0 + row;
-                    const int off = (r < M && k < K) ? (r * K + k) * ESZ : kOOB;
-                    __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, dst, 16, off, 0, 0, 0);
-                } else {
-                    const int r = n0 + row - TL::BM;
-                    const int off = (r < N && k < K) ? (r * K + k) * ESZ : kOOB;
-                    __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, dst, 16, off, 0, 0, 0);
-                }
-            }
+            lds_t* dst = (lds_t*)(lds + (ins < NI ? buf * SB + ins * 1024 : STAGES * SB));
+            const int off = dma_off[q] == kOOB ? kOOB : dma_off[q] + k0 * ESZ;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(q < 2 ? xr : wr, dst, 16, off, 0, 0, 0);
         }
     };
     // this wave's DMA instructions per stage
-    const int per_stage = (NI - wave + NW - 1) / NW;
+    constexpr int per_stage = IPW;
     // fragment read offset of lane (g, i): group g of row i sits in slot g ^ f(i)
     const int frag_off = i * 64 + 16 * (g ^ (((i >> 1) ^ (i >> 3)) & 3));
 
@@ -415,10 +425,46 @@ __global__ __launch_bounds__(TL::NT) void gemm_lse_partials_dma(
         if (kt_ + STAGES - 1 < nk) issue((kt_ + STAGES - 1) % STAGES, (kt_ + STAGES - 1) * BK);                  \
         stage_ready(kt_ + 2, nk - 1 < kt_ + STAGES - 1 ? nk - 1 : kt_ + STAGES - 1);                            \
     }
-    for (int kt = 0; kt < nk; kt += 2) {  // nk is even (K % 64 == 0 on this path)
+    // Steady state (every step sends a DMA and waits for the stage two ahead with one stage in
+    // flight behind it): the DMA goes first, then this stage's MFMA work with the next stage's
+    // fragment reads, then a fixed vmcnt and the barrier -- no branches in the step. Stage
+    // kt + STAGES - 1 goes into the buffer of stage kt - 1, whose fragments were read during
+    // step kt - 2 and consumed by step kt - 1's MFMAs, before the last barrier.
+#define FCONV_DMA_STEADY(KT, AC, BC, AN, BN_)                                                                    \
+    {                                                                                                            \
+        const int kt_ = (KT);                                                                                    \
+        issue((kt_ + STAGES - 1) % STAGES, (kt_ + STAGES - 1) * BK);                                             \
+        _Pragma("unroll") for (int j = 0; j < TL::MB; ++j) AN[j] = frag_a(kt_ + 1, j);                           \
+        _Pragma("unroll") for (int j = 0; j < TL::NB; ++j) BN_[j] = frag_b(kt_ + 1, j);                          \
+        if constexpr (TL::BF16) {                                                                                \
+            _Pragma("unroll") for (int jm = 0; jm < TL::MB; ++jm)                                                \
+                _Pragma("unroll") for (int jn = 0; jn < TL::NB; ++jn)                                            \
+                    acc[jm][jn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, AC[jm]),     \
+                        __builtin_bit_cast(bf16x8, BC[jn]), acc[jm][jn], 0, 0, 0);                                \
+        } else {                                                                                                 \
+            _Pragma("unroll") for (int s_ = 0; s_ < 4; ++s_)                                                     \
+                _Pragma("unroll") for (int jm = 0; jm < TL::MB; ++jm)                                            \
+                    _Pragma("unroll") for (int jn = 0; jn < TL::NB; ++jn)                                        \
+                        acc[jm][jn] = __builtin_amdgcn_mfma_f32_16x16x4f32(AC[jm][s_], BC[jn][s_], acc[jm][jn],  \
+                            0, 0, 0);                                                                            \
+        }                                                                                                        \
+        dma_step_schedule<TL::MB + TL::NB, TL::MB * TL::NB * (TL::BF16 ? 1 : 4)>();                              \
+        __asm__ volatile("" ::: "memory");                                                                       \
+        __builtin_amdgcn_s_waitcnt(0x0F70 | per_stage);  /* vmcnt(per_stage): stage kt + 2 landed */            \
+        __builtin_amdgcn_s_barrier();                                                                            \
+        __asm__ volatile("" ::: "memory");                                                                       \
+    }
+    static_assert(STAGES == 4, "steady-state waits count one stage in flight");
+    int kt = 0;
+    for (; kt + 2 * (STAGES - 1) <= nk; kt += 2) {  // both steps send a DMA (nk is even on this path)
+        FCONV_DMA_STEADY(kt, a0, b0, a1, b1)
+        FCONV_DMA_STEADY(kt + 1, a1, b1, a0, b0)
+    }
+    for (; kt < nk; kt += 2) {  // the last steps: fewer DMAs, shrinking waits
         FCONV_DMA_STEP(kt, a0, b0, a1, b1)
         FCONV_DMA_STEP(kt + 1, a1, b1, a0, b0)
     }
+#undef FCONV_DMA_STEADY
 #undef FCONV_DMA_STEP
     __syncthreads();  // every wave is done with the stage buffers (the epilogue reuses them)
     tile_epilogue<TL>(acc, (float2*)lds, bias, part, m0, n0, M, N, tn, tilesN, scale, cmin, cmax, tid, g, i, wn, rm0,
