@@ -55,6 +55,24 @@ struct GTile {
     static_assert(KG % 4 == 0, "whole MFMA K steps per stage");
 };
 
+// Tile order. The dispatcher deals workgroups to the eight XCDs round-robin (workgroup b
+// runs on XCD b % 8), and each XCD has its own L2. When the tile count is a multiple of 8,
+// workgroup b is renumbered to logical tile (b % 8) * (T / 8) + b / 8, so each XCD holds a
+// contiguous run of T / 8 logical tiles; logical tiles are then walked in groups of
+// kGroupM tile rows (column by column inside a group), so one XCD's run is a block of
+// kGroupM x (T / 8 / kGroupM) tiles that shares kGroupM strips of x and the W strips of
+// its columns in that XCD's L2.
+constexpr int kGroupM = 4;
+
+__device__ __forceinline__ void tile_coords(int b, int tilesM, int tilesN, int& tm, int& tn) {
+    const int T = tilesM * tilesN, per = T >> 3;
+    const int L = b < (per << 3) ? (b & 7) * per + (b >> 3) : b;
+    const int span = kGroupM * tilesN, first = (L / span) * kGroupM;
+    const int rows = min(kGroupM, tilesM - first), r = L - (L / span) * span;
+    tm = first + r % rows;
+    tn = r / rows;
+}
+
 // 256 x 192 tiles: 2048 x 6144 is exactly 256 tiles, one per CU; 8 waves of 64 x 96.
 using GTileF = GTile<256, 192, 4, 2, 32, 512, false>;
 using GTileH = GTile<256, 192, 4, 2, 64, 512, true>;
@@ -167,7 +185,8 @@ __global__ __launch_bounds__(TL::NT) void gemm_lse_partials(
     __shared__ f4 As[2][TL::BM * kPitch];
     __shared__ f4 Bs[2][TL::BN * kPitch];
 
-    const int tn = blockIdx.x % tilesN, tm = blockIdx.x / tilesN;
+    int tm, tn;
+    tile_coords(blockIdx.x, (int)gridDim.x / tilesN, tilesN, tm, tn);
     const int m0 = tm * TL::BM, n0 = tn * TL::BN;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int g = lane >> 4, i = lane & 15;
@@ -299,7 +318,8 @@ __global__ __launch_bounds__(TL::NT) void gemm_lse_partials_dma(
     static_assert(ROWS % 16 == 0 && TL::BM % 16 == 0, "whole 16-row DMA blocks");
     __shared__ __attribute__((aligned(1024))) unsigned char lds[STAGES * SB + 1024];  // + junk DMA target
 
-    const int tn = blockIdx.x % tilesN, tm = blockIdx.x / tilesN;
+    int tm, tn;
+    tile_coords(blockIdx.x, (int)gridDim.x / tilesN, tilesN, tm, tn);
     const int m0 = tm * TL::BM, n0 = tn * TL::BN;
     const int tid = threadIdx.x, lane = tid & 63;
     // The wave index is the same in every lane; readfirstlane makes that visible to the

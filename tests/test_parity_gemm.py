@@ -34,10 +34,11 @@ def rand_case(seed, M, K, N, wb=None, dtype="f32"):
 # K % 32 == 0 (fp32) / K % 64 == 0 (bf16) with 16-byte aligned operands takes the LDS-DMA
 # kernel; (300, 32, 385) is its shortest K (one pair of stages) with ragged rows and columns
 # over two tile rows and three tile columns, (513, 96, 400) three tile rows and an odd
-# number of stage pairs.
+# number of stage pairs. (1300, 64, 1000) has 6 x 6 tiles: the first 32 are renumbered per
+# XCD and the last 4 are not, and the second group of tile rows is two rows short.
 @pytest.mark.parametrize("M,K,N", [(37, 19, 53), (1, 1, 1), (5, 4, 3), (128, 128, 128), (130, 260, 300),
                                    (64, 1000, 129), (257, 33, 1000), (3, 4096, 6144), (300, 32, 385),
-                                   (513, 96, 400)])
+                                   (513, 96, 400), (1300, 64, 1000)])
 @pytest.mark.parametrize("scale,cmin,cmax", [(4.0, -10.0, 10.0), (4.0, -0.25, 0.5), (-3.0, -1e30, 1e30)])
 def test_gemm_small_shapes(M, K, N, scale, cmin, cmax):
     X, W, b = rand_case(M + K + N, M, K, N)
@@ -50,7 +51,7 @@ def test_gemm_small_shapes(M, K, N, scale, cmin, cmax):
 
 @pytest.mark.parametrize("M,K,N", [(37, 19, 53), (1, 1, 1), (5, 8, 3), (128, 128, 128), (130, 264, 300),
                                    (64, 1000, 129), (257, 33, 1000), (3, 4096, 6144), (300, 72, 385),
-                                   (300, 64, 385), (513, 192, 400)])
+                                   (300, 64, 385), (513, 192, 400), (1300, 64, 1000)])
 @pytest.mark.parametrize("scale,cmin,cmax", [(4.0, -10.0, 10.0), (-3.0, -1e30, 1e30)])
 def test_gemm_bf16_small_shapes(M, K, N, scale, cmin, cmax):
     # K % 8 != 0 takes the element-wise load path, K % 8 == 0 the 16-byte one
