@@ -27,6 +27,8 @@ SHAPES = [
     (1, 17, 9, 40, 65),    # Cin one past an fp32 chunk, Cout one past an oc tile
     (1, 3, 5, 5, 2),       # tiny map
     (2, 33, 20, 37, 16),   # Cin one past a bf16 chunk
+    (1, 40, 19, 45, 200),  # bf16 128-channel tiles: a ragged second tile, element-wise halo
+    (1, 64, 17, 48, 144),  # bf16 128-channel tiles: 16 channels in the second tile, 16-byte halo runs
 ]
 
 
