@@ -79,10 +79,16 @@ struct GeoHalo {
 
     __device__ __forceinline__ void setup(int, int, int, int) {}
 
+    __device__ __forceinline__ static bool last_used(int tid) {
+        return ITEMS % TL::NT == 0 || (__builtin_amdgcn_readfirstlane(tid) & ~63) + (PER - 1) * TL::NT < ITEMS;
+    }
+
+    template <bool WITH_LAST = true>
     __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t xr, int H, int W, int Cin, int c0, int ih0,
                                          int iw0, int tid) {
 #pragma unroll
         for (int j = 0; j < PER; ++j) {
+            if (!WITH_LAST && j == PER - 1) continue;  // no lane of this wave holds an item in round j
             const int it = tid + j * TL::NT;
             const int q = it & 3, pos = it >> 2;
             const int r = pos / TL::HC, col = pos % TL::HC;
@@ -170,6 +176,14 @@ struct GeoHaloVec {
     // per channel remain. Offsets past the image read as zero: a run outside the rows or
     // columns starts at kOOB (kOOB + e * plane stays below 2^32 because the image is under
     // 2^31 bytes), and in a chunk that runs past Cin each missing channel takes kOOB.
+    // Whether any lane of this wave holds an item in the last round (j = PER - 1); only that
+    // round can be short. A wave without one issues none of its loads: an out-of-range load
+    // costs the texture unit as much as a real one. Uniform across the wave.
+    __device__ __forceinline__ static bool last_used(int tid) {
+        return ITEMS % TL::NT == 0 || (__builtin_amdgcn_readfirstlane(tid) & ~63) + (PER - 1) * TL::NT < ITEMS;
+    }
+
+    template <bool WITH_LAST = true>
     __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t xr, int H, int W, int Cin, int c0, int ih0, int a0,
                                          int tid) {
         (void)tid;
@@ -178,6 +192,7 @@ struct GeoHaloVec {
         const bool full = c0 + Elem<BF16>::CK <= Cin;
 #pragma unroll
         for (int j = 0; j < PER; ++j) {
+            if (!WITH_LAST && j == PER - 1) continue;
             const int ih = ih0 + lane_rs[j];
             const bool ok = ((col_ok >> j) & 1u) && (unsigned)ih < (unsigned)H;
             const unsigned b = ok ? (unsigned)(lane_off[j] + step) * ESZ : (unsigned)kOOB;
@@ -351,19 +366,51 @@ __global__ __launch_bounds__(TL::NT) __attribute__((amdgpu_waves_per_eu(TL::OCC)
         else hs.store(halo, tid);
     };
     hs.setup(H, W, hcol0, tid);
+    const bool last_used = Halo::last_used(tid);
     hs.load(xr, H, W, Cin, 0, oh0 * S - pad, hcol0, tid);
     wsg.load(wr, CoutPad, 0, oc0, tid);
+    // The next step's loads are spread between this step's MFMAs instead of issued as one
+    // burst: the texture unit takes a 16-byte-per-lane load every ~16 cycles, so a burst from
+    // every wave stalled each wave ~1.5-2.3 k cycles in issue before its first MFMA.
+    constexpr int kMfmaPerStep = KS * TL::WPB * TL::WOB * (BF16 ? 1 : 4);
+    constexpr int kLoadsPerStep = Halo::PER * Elem<BF16>::EPG + GeoWeights<BF16, TL>::PER;
+    constexpr int kMfmaPerLoad = kMfmaPerStep / kLoadsPerStep > 0 ? kMfmaPerStep / kLoadsPerStep : 1;
+    // Only the 8-wave bf16 tile with 16-byte runs and K < 5: elsewhere it made the compiler spill.
+    constexpr bool kInterleave = BF16 && VEC && TL::WO == 2 && KS < 5;
     for (int st = 0; st < nStep; ++st) {
         if (st) __syncthreads();  // every wave is done reading the previous step
         halo_store();
         wsg.store(wl, tid);
         __syncthreads();
-        if (st + 1 < nStep) {
-            const int c = (st + 1) / KS, kh = (st + 1) % KS;
-            hs.load(xr, H, W, Cin, c * CK, oh0 * S + kh - pad, hcol0, tid);
-            wsg.load(wr, CoutPad, (c * KS + kh) * KS, oc0, tid);
+        if constexpr (kInterleave) {
+            if (st + 1 < nStep) {
+                const int c = (st + 1) / KS, kh = (st + 1) % KS;
+                // loads and MFMAs in one basic block, so the scheduler can interleave them; a
+                // wave with no halo item in its last round leaves those loads out
+                auto load_and_compute = [&](auto with_last) {
+                    hs.template load<decltype(with_last)::value>(xr, H, W, Cin, c * CK, oh0 * S + kh - pad, hcol0,
+                                                                 tid);
+                    wsg.load(wr, CoutPad, (c * KS + kh) * KS, oc0, tid);
+                    compute_step();
+#pragma unroll
+                    for (int k = 0; k < kLoadsPerStep; ++k) {
+                        __builtin_amdgcn_sched_group_barrier(0x008, kMfmaPerLoad, 0);  // MFMA
+                        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);             // VMEM read
+                    }
+                };
+                if (last_used) load_and_compute(std::true_type{});
+                else load_and_compute(std::false_type{});
+            } else {
+                compute_step();
+            }
+        } else {
+            if (st + 1 < nStep) {
+                const int c = (st + 1) / KS, kh = (st + 1) % KS;
+                hs.load(xr, H, W, Cin, c * CK, oh0 * S + kh - pad, hcol0, tid);
+                wsg.load(wr, CoutPad, (c * KS + kh) * KS, oc0, tid);
+            }
+            compute_step();
         }
-        compute_step();
     }
 
     // Epilogue. Lane (g, i) register r holds pixel 4g + r of the pixel block and output
