@@ -114,8 +114,12 @@ struct HaloVec {
         }
     }
 
-    __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t xr, int H, int W, int Cin, int c0, int oh0,
-                                         int ow0, int tid) {
+    // Per-thread part of the run addresses, fixed for the whole K loop: the byte offset of
+    // the item's run at channel 0, or kOOB when its halo row or columns lie outside the
+    // image (the tile's position does not change between chunks).
+    unsigned lane_b[PER];
+
+    __device__ __forceinline__ void setup(int H, int W, int oh0, int ow0, int tid) {
 #pragma unroll
         for (int j = 0; j < PER; ++j) {
             const int it = tid + j * TL::NT;
@@ -123,11 +127,27 @@ struct HaloVec {
             item(it, q, cg, r);
             const int ih = oh0 + r, iw = ow0 + cg * VW;
             const bool inb = it < ITEMS && ih < H && iw < W;
-            const int base = ((c0 + q * EPG) * H + ih) * W + iw;
+            lane_b[j] = inb ? (unsigned)(((q * EPG) * H + ih) * W + iw) * ESZ : (unsigned)kOOB;
+        }
+    }
+
+    // Chunk at channel c0: channel c of a run is lane_b + c * plane bytes. A run outside
+    // the image stays at or past kOOB, and below 2^32 because the image is under 2^31
+    // bytes; a channel past Cin (the last chunk only) takes kOOB.
+    __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t xr, int H, int W, int Cin, int c0, int oh0,
+                                         int ow0, int tid) {
+        (void)oh0;
+        (void)ow0;
+        const unsigned plane_b = (unsigned)(H * W) * ESZ;
+        const bool full = c0 + Elem<BF16>::CK <= Cin;
+#pragma unroll
+        for (int j = 0; j < PER; ++j) {
+            const unsigned b = lane_b[j] + (unsigned)c0 * plane_b;
+            const int cb = c0 + ((tid + j * TL::NT) & 3) * EPG;
 #pragma unroll
             for (int e = 0; e < EPG; ++e) {
-                const bool ok = inb && c0 + q * EPG + e < Cin;
-                v[j][e] = __builtin_amdgcn_raw_buffer_load_b128(xr, ok ? (base + e * H * W) * ESZ : kOOB, 0, 0);
+                const unsigned off = (full || cb + e < Cin) ? b + e * plane_b : (unsigned)kOOB;
+                v[j][e] = __builtin_amdgcn_raw_buffer_load_b128(xr, (int)off, 0, 0);
             }
         }
     }
@@ -170,6 +190,8 @@ struct HaloScalar {
     static constexpr int ITEMS = TL::HR * TL::HC * 4;
     static constexpr int PER = (ITEMS + TL::NT - 1) / TL::NT;
     u4 v[PER];
+
+    __device__ __forceinline__ void setup(int, int, int, int, int) {}
 
     __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t xr, int H, int W, int Cin, int c0, int oh0,
                                          int ow0, int tid) {
@@ -333,6 +355,7 @@ __global__ __launch_bounds__(TL::NT) __attribute__((amdgpu_waves_per_eu(TL::MINW
     WeightStage<BF16, TL> wsg;
     // One chunk ahead: the next chunk's loads fly while this chunk computes.
     Halo hs;
+    hs.setup(H, W, oh0, ow0, tid);
     hs.load(xr, H, W, Cin, 0, oh0, ow0, tid);
     wsg.load(wr, CoutPad, 0, oc0, tid);
     for (int ch = 0; ch < nChunk; ++ch) {
@@ -405,6 +428,14 @@ __global__ __launch_bounds__(TL::NT) __attribute__((amdgpu_waves_per_eu(TL::MINW
             if (oc < Cout) dst[((long long)n * nTiles + th * tilesW + tw) * Cout + oc] = s;
         }
     } else {
+        // Every store address is the lane's base plus uniform offsets: block jp sits
+        // pb_row(pb) - pb_row(pb0) rows and pb_col(pb) - pb_col(pb0) column blocks from the
+        // wave's first block pb0, and oc block jo 16 OH OW elements on.
+        const int pb0 = wpi * TL::WPB;
+        const int oc_w = oc0 + woi * TL::WOB * 16 + i;
+        float* const obase = dst + (((long long)n * Cout + oc_w) * OH + oh0 + pb_row(pb0)) * OW + ow0 +
+                             pb_col(pb0) * 16 + 4 * g;
+        const long long oc_stride = 16LL * OH * OW;
 #pragma unroll
         for (int jp = 0; jp < TL::WPB; ++jp) {
             const int pb = wpi * TL::WPB + jp;
@@ -413,12 +444,12 @@ __global__ __launch_bounds__(TL::NT) __attribute__((amdgpu_waves_per_eu(TL::MINW
             if (oh >= OH) continue;
 #pragma unroll
             for (int jo = 0; jo < TL::WOB; ++jo) {
-                const int oc = oc0 + (woi * TL::WOB + jo) * 16 + i;
-                if (oc >= Cout) continue;
+                if (oc_w + jo * 16 >= Cout) continue;
                 float v[4];
 #pragma unroll
                 for (int r = 0; r < 4; ++r) v[r] = activate<ACT>(acc[jp][jo][r]);
-                float* o = dst + (((long long)n * Cout + oc) * OH + oh) * OW + owb;
+                float* o = obase + jo * oc_stride + (long long)(pb_row(pb) - pb_row(pb0)) * OW +
+                           (pb_col(pb) - pb_col(pb0)) * 16;
                 // out_align: 16 / 8 / 4 = byte alignment of the output base pointer
                 if ((OW & 3) == 0 && out_align >= 16 && owb + 3 < OW) {
                     *(f4*)o = f4{v[0], v[1], v[2], v[3]};
