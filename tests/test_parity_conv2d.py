@@ -29,6 +29,7 @@ SHAPES = [
     (2, 33, 20, 37, 16),   # Cin one past a bf16 chunk
     (1, 40, 19, 45, 200),  # bf16 128-channel tiles: a ragged second tile, element-wise halo
     (1, 64, 17, 48, 144),  # bf16 128-channel tiles: 16 channels in the second tile, 16-byte halo runs
+    (1, 8, 11, 24, 129),   # 128-channel tiles: one channel in the second tile
 ]
 
 
@@ -123,3 +124,34 @@ def test_conv2d_full_size_1x1_full_output_whole():
         worst = max(worst, err)
         assert err <= TOL_F32, (n, err)
     print(f"{name}: all {out.numel()} outputs, err={worst:.3e}", flush=True)
+
+
+def _random_case(rng):
+    K = int(rng.choice([1, 3, 5]))
+    S = int(rng.choice([1, 2]))
+    P = int(rng.integers(0, K))
+    N = int(rng.integers(1, 3))
+    Cin = int(rng.integers(1, 70))
+    Cout = int(rng.choice([int(rng.integers(1, 70)), int(rng.integers(120, 300))]))
+    H = int(rng.integers(max(1, K - 2 * P), 40))
+    W = int(rng.choice([int(rng.integers(max(1, K - 2 * P), 70)), 8 * int(rng.integers(1, 9))]))
+    W = max(W, K - 2 * P)
+    return K, S, P, N, Cin, H, W, Cout, bool(rng.integers(0, 2)), int(rng.integers(0, 4)), int(rng.integers(0, 2))
+
+
+@pytest.mark.parametrize("seed", range(24))
+def test_conv2d_random_shapes(seed):
+    # seeded random geometry, sizes, dtype, activation and pool mode: sizes cross the tile,
+    # chunk and channel-tile boundaries at random, and W is often a multiple of 8 so the
+    # 16-byte halo paths run as well as the element-wise ones
+    rng = np.random.default_rng(7000 + seed)
+    K, S, P, N, Cin, H, W, Cout, bf16, act, pool = _random_case(rng)
+    print(f"seed={seed} K={K} S={S} P={P} x=({N},{Cin},{H},{W}) Cout={Cout} bf16={bf16} act={act} pool={pool}",
+          flush=True)
+    x, w, b = rand_case(100 + seed, N, Cin, H, W, Cout, K, bf16=bf16)
+    got = run_conv2d(x, w, b, S, P, ACTS[act], pool, bf16)
+    ref = oracle.conv2d_act_pool(x, w, b, S, P, ACTS[act], pool)
+    err = max_rel_err(got, ref)
+    print(f"  err={err:.3e}", flush=True)
+    assert err <= (TOL_BF16 if bf16 else TOL_F32)
+    assert err <= TOL_BF16_ARITH
