@@ -192,3 +192,25 @@ def test_concurrent_streams_bit_equal():
         assert torch.equal(o, ref_b)
     for o in outs[2]:
         assert torch.equal(o, ref_g)
+
+
+@pytest.mark.parametrize("seed", range(16))
+def test_gemm_random_shapes(seed):
+    # seeded random sizes (K often a multiple of the 64-byte stage so the LDS-DMA path runs,
+    # otherwise the register-staged one), scale and clamp window, either dtype
+    rng = np.random.default_rng(8000 + seed)
+    dtype = "bf16" if rng.integers(0, 2) else "f32"
+    M = int(rng.integers(1, 700))
+    N = int(rng.integers(1, 1500))
+    stage = 32 if dtype == "bf16" else 16
+    K = int(rng.choice([int(rng.integers(1, 400)), stage * 2 * int(rng.integers(1, 12))]))
+    scale = float(rng.choice([4.0, -2.5, 0.5]))
+    cmin = float(rng.uniform(-12.0, 0.0))
+    cmax = float(cmin + rng.uniform(0.0, 20.0))
+    print(f"seed={seed} {dtype} M={M} K={K} N={N} scale={scale} clamp=[{cmin:.3f},{cmax:.3f}]", flush=True)
+    X, W, b = rand_case(500 + seed, M, K, N, dtype=dtype)
+    got = run_gemm(X, W, b, scale, cmin, cmax)
+    ref, _ = oracle.gemm_lse_mish(X, W, b, scale, cmin, cmax)
+    err = max_rel_err(got, ref)
+    print(f"  err={err:.3e}", flush=True)
+    assert err <= TOL_F32
