@@ -13,14 +13,12 @@ __device__ __forceinline__ float fast_exp(float v) {
     return __builtin_amdgcn_exp2f(v * 1.4426950408889634f);
 }
 
-// max(v, 0) and min(v, 20) as one v_med3_f32 each. On an MFMA accumulator fmaxf / fminf also
-// emit a canonicalizing v_max_f32 v, v (the compiler cannot tell the value is not a
-// signalling NaN), one more VALU instruction per output in every epilogue; with an infinite
-// bound the compiler turns the med3 back into that pair, so the bounds are +-FLT_MAX. Equal to
-// max / min for every finite v.
+// max(v, 0) as one v_med3_f32. On an MFMA accumulator fmaxf also emits a canonicalizing
+// v_max_f32 v, v (the compiler cannot tell the value is not a signalling NaN), one more VALU
+// instruction per output in every epilogue; with an infinite bound the compiler turns the med3
+// back into that pair, so the upper bound is FLT_MAX. Equal to max(v, 0) for every finite v.
 constexpr float kFltMax = 3.402823466e38f;
 __device__ __forceinline__ float relu(float v) { return __builtin_amdgcn_fmed3f(v, 0.0f, kFltMax); }
-__device__ __forceinline__ float min20(float v) { return __builtin_amdgcn_fmed3f(v, -kFltMax, 20.0f); }
 
 // Exact-form GELU, 0.5 v (1 + erf(v / sqrt 2)) = v Phi(v) ("Kimi-K2.6 l2_p67" page:
 // PyTorch's default approximate='none' form, not the tanh approximation).
@@ -58,14 +56,16 @@ __device__ __forceinline__ float gelu_tanh(float v) {
 
 // Mish(v) = v tanh(softplus(v)). With t = e^v, tanh(log(1 + t)) = q / (q + 2), q = t (t + 2),
 // so mish(v) = v - v r with r = 2 / (q + 2) = 1 / (1 + t (1 + t / 2)): one exponential, one
-// reciprocal and five VALU operations (the product form v q / (q + 2) takes seven; in the
-// fp32 convolutions, where VALU work serializes with the MFMAs, the Mish∘Mish workloads ran
-// ~1 % faster this way). t is taken at min(v, 20): for v > 20, r < 1e-17 and the result is v;
-// for very negative v, t underflows to 0, r to 1 and the result to 0, as the exact function
-// tends. The subtraction gives up relative (not absolute) accuracy where mish(v) is tiny
-// (v << 0): the result stays within 1.3e-6 of the exact Mish for every v.
+// reciprocal and four VALU operations (the product form v q / (q + 2) takes seven; in the
+// fp32 convolutions, where VALU work serializes with the MFMAs, each one saved per output is
+// kernel time). Large v needs no clamp: for v > 20, r < 1e-17 and v - v r rounds to v; from
+// v ~ 44 on, t (1 + t / 2) overflows to +inf (and from v ~ 88 on t itself), r is 0 and the
+// result is exactly v. For very negative v, t underflows to 0, r to 1 and the result to 0,
+// as the exact function tends. The subtraction gives up relative (not absolute) accuracy
+// where mish(v) is tiny (v << 0): the result stays within 1.3e-6 of the exact Mish for
+// every finite v.
 __device__ __forceinline__ float mish_f32(float v) {
-    const float t = fast_exp(min20(v));
+    const float t = fast_exp(v);
     const float r = __builtin_amdgcn_rcpf(fmaf(t, fmaf(t, 0.5f, 1.0f), 1.0f));
     return fmaf(-v, r, v);
 }
