@@ -1,4 +1,4 @@
-"""The device erf-GELU's polynomial, checked on the CPU (no GPU).
+"""The device activation formulas, checked on the CPU (no GPU).
 
 ``gelu_erf`` in csrc/device_math.h evaluates the exact-form GELU as max(v, 0) - |v| 2^Q(|v|),
 with Q a degree-5 polynomial standing for log2 Phi(-|v|). These tests read the
@@ -7,6 +7,10 @@ per fused multiply-add, a correctly rounded 2^x) and hold it to the bound its co
 against the exact GELU v Phi(v) from scipy's normal CDF. They also check that Q falls
 monotonically for every a >= 0, which the device relies on for large |v|, and that
 gelu_fit.py still reproduces the coefficients.
+
+``mish_f32`` evaluates mish(v) = v - v r, r = 1 / (1 + t (1 + t/2)), t = e^v, with no clamp on
+v: the last test emulates that form in fp32 and checks the header's claims, |error| <= 1.3e-6
+for every finite v and exactly v once t (1 + t/2) overflows.
 """
 import os
 import re
@@ -76,3 +80,31 @@ def test_gelu_fit_reproduces_header():
     c, err = fit()
     assert err < 5e-7
     np.testing.assert_allclose(np.float32(c), header_coefficients(), rtol=1e-5)
+
+
+def device_mish(v32):
+    """fp32 emulation of mish_f32: t = 2^(v log2 e), r = 1 / fma(t, fma(t, 0.5, 1), 1), fma(-v, r, v)."""
+    v = v32.astype(np.float64)
+    with np.errstate(over="ignore", invalid="ignore"):
+        s = (v * np.float64(np.float32(1.4426950408889634))).astype(np.float32).astype(np.float64)
+        t = np.exp2(s).astype(np.float32).astype(np.float64)
+        a = (t * 0.5 + 1.0).astype(np.float32).astype(np.float64)
+        b = (t * a + 1.0).astype(np.float32).astype(np.float64)
+        r = (1.0 / b).astype(np.float32).astype(np.float64)
+        return (-v * r + v).astype(np.float32).astype(np.float64)
+
+
+def test_device_mish_form_without_clamp():
+    src = open(HEADER).read()
+    body = src[src.index("float mish_f32(float v)"):]
+    body = body[:body.index("\n}\n")]
+    assert "fast_exp(v)" in body and "min" not in body  # the form emulated below
+    v = np.concatenate([np.linspace(-60, 120, 1_800_001), np.logspace(1, 38, 4000),
+                        -np.logspace(1, 38, 4000)]).astype(np.float32)
+    vd = v.astype(np.float64)
+    exact = vd * np.tanh(np.maximum(vd, 0) + np.log1p(np.exp(-np.abs(vd))))
+    got = device_mish(v)
+    assert np.isfinite(got).all()
+    assert np.abs(got - exact).max() <= 1.3e-6
+    big = vd > 45  # t (1 + t / 2) overflows: r = 0 and the result is v itself
+    assert np.array_equal(got[big], vd[big])
