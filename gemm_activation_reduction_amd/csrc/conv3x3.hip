@@ -72,6 +72,11 @@ using TileA = Tile<8, 32, 64, 4, 1, 2, 256>;
 // bf16: the same tile shape (measured on MI355X: a 256 x 128 tile with 8 waves and one
 // workgroup per CU, or 32-oc tiles with 3 workgroups per CU, were both slower).
 using TileB = Tile<8, 32, 64, 4, 1, 2, 256>;
+// Layers with at most 16 or 32 output channels take a tile of that many channels (same
+// pixels, same waves, one or two oc blocks per wave): a 64-channel tile would spend 4x or 2x
+// the MFMA work, weight staging and latency per workgroup on padding channels.
+using TileS16 = Tile<8, 32, 16, 4, 1, 2, 256>;
+using TileS32 = Tile<8, 32, 32, 4, 1, 2, 256>;
 
 
 // ---------------------------------------------------------------------------------
@@ -844,7 +849,8 @@ ConvPlan plan_conv(bool bf16, int act, int pool, int N, int Cin, int H, int W, i
     p.wide = bf16 && vec && Cout >= TileW::BN;
     p.TH = p.wide ? TileW::TH : bf16 ? TileB::TH : TileA::TH;
     p.TW = p.wide ? TileW::TW : bf16 ? TileB::TW : TileA::TW;
-    p.BN = p.wide ? TileW::BN : bf16 ? TileB::BN : TileA::BN;
+    p.BN = p.wide ? TileW::BN : Cout <= TileS16::BN ? TileS16::BN : Cout <= TileS32::BN ? TileS32::BN
+                                                                 : bf16 ? TileB::BN : TileA::BN;
     p.CK = bf16 ? Elem<true>::CK : Elem<false>::CK;
     p.tilesH = (p.OH + p.TH - 1) / p.TH;
     p.tilesW = (p.OW + p.TW - 1) / p.TW;
@@ -877,9 +883,17 @@ hipError_t launch_conv(const ConvPlan& p, const void* x, const void* w, const fl
     float* dst = p.pool ? part : out;
     const char* kname = p.wide ? "conv3x3_wide_bf16" : "conv3x3_fused";
     if (timer) timer->begin(kname, stream);
-    e = p.wide   ? launch_wide(p, x, wpk, b, dst, stream)
-        : p.bf16 ? launch_act<true, TileB>(p, x, wpk, b, dst, stream)
-                 : launch_act<false, TileA>(p, x, wpk, b, dst, stream);
+    if (p.wide)
+        e = launch_wide(p, x, wpk, b, dst, stream);
+    else if (p.BN == TileS16::BN)
+        e = p.bf16 ? launch_act<true, TileS16>(p, x, wpk, b, dst, stream)
+                   : launch_act<false, TileS16>(p, x, wpk, b, dst, stream);
+    else if (p.BN == TileS32::BN)
+        e = p.bf16 ? launch_act<true, TileS32>(p, x, wpk, b, dst, stream)
+                   : launch_act<false, TileS32>(p, x, wpk, b, dst, stream);
+    else
+        e = p.bf16 ? launch_act<true, TileB>(p, x, wpk, b, dst, stream)
+                   : launch_act<false, TileA>(p, x, wpk, b, dst, stream);
     if (timer) timer->end(kname, stream);
     if (e != hipSuccess || !p.pool) return e;
     if (timer) timer->begin("pool_finalize", stream);
