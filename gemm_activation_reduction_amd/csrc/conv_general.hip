@@ -49,13 +49,17 @@ constexpr int kGRow = 80;  // bytes per LDS row: 64 bytes of channel data + 16 o
 
 // WO = 1: 64 output channels per workgroup, 4 waves. WO = 2: 128 output channels, 8 waves
 // (4 pixel groups x 2 channel halves): the staged halo of a step feeds twice the MFMAs, so
-// the halo bytes moved through the vector memory path per MFMA halve.
-template <int KS_, int S_, int WO_ = 1, int OCC_ = 2>
+// the halo bytes moved through the vector memory path per MFMA halve. BN_ = 32 (with WO = 1)
+// is the tile of layers with at most 32 output channels: 4 waves of 4 pixel blocks x 2 oc
+// blocks, so a narrow layer does not spend MFMA work and weight staging on 32 padding
+// channels.
+template <int KS_, int S_, int WO_ = 1, int OCC_ = 2, int BN_ = 64 * WO_>
 struct GeoTile {
     static constexpr int KS = KS_, S = S_, WO = WO_;
     static constexpr int OCC = OCC_;                            // waves per SIMD the registers are fit to
-    static constexpr int TH = 8, TW = 32, BN = 64 * WO, NT = 256 * WO;
-    static constexpr int WP = 4;                                // pixel wave groups; each wave 4 x 4 blocks
+    static constexpr int TH = 8, TW = 32, BN = BN_, NT = 256 * WO;
+    static_assert(BN % (16 * WO) == 0 && BN <= 64 * WO, "whole oc blocks per wave");
+    static constexpr int WP = 4;                                // pixel wave groups; each wave 4 pixel blocks
     static constexpr int CB = TW / 16, PB = TH * CB, OB = BN / 16, WPB = PB / WP, WOB = OB / WO;
     static constexpr int HC = (TW - 1) * S + KS;                // input columns per staged row
     static constexpr int HCS = (HC + S - 1) / S;                // positions per column-parity plane
@@ -557,7 +561,7 @@ ConvPlan plan_conv_general(bool bf16, int act, int pool, int N, int Cin, int H, 
     p.OW = (W + 2 * pad - K) / stride + 1;
     p.TH = 8; p.TW = 32;
     // 128 channels per workgroup (8 waves) where the halo traffic per MFMA is the limit
-    p.BN = (bf16 || K == 1) && Cout >= 128 ? 128 : 64;
+    p.BN = (bf16 || K == 1) && Cout >= 128 ? 128 : Cout <= 32 ? 32 : 64;
     p.CK = bf16 ? Elem<true>::CK : Elem<false>::CK;
     p.tilesH = (p.OH + p.TH - 1) / p.TH;
     p.tilesW = (p.OW + p.TW - 1) / p.TW;
@@ -603,6 +607,16 @@ hipError_t launch_conv_general(const ConvPlan& p, const void* x, const void* w, 
     } else if (p.BN == 128 && p.KS == 1) {
         e = p.stride == 1 ? launch_geo_act<false, GeoTile<1, 1, 2>>(p, x, wpk, b, dst, stream)
                           : launch_geo_act<false, GeoTile<1, 2, 2>>(p, x, wpk, b, dst, stream);
+    } else if (p.BN == 32) {
+        switch (p.KS * 10 + p.stride) {
+            case 11: e = launch_geo_dtype<GeoTile<1, 1, 1, 2, 32>>(p, x, wpk, b, dst, stream); break;
+            case 12: e = launch_geo_dtype<GeoTile<1, 2, 1, 2, 32>>(p, x, wpk, b, dst, stream); break;
+            case 31: e = launch_geo_dtype<GeoTile<3, 1, 1, 2, 32>>(p, x, wpk, b, dst, stream); break;
+            case 32: e = launch_geo_dtype<GeoTile<3, 2, 1, 2, 32>>(p, x, wpk, b, dst, stream); break;
+            case 51: e = launch_geo_dtype<GeoTile<5, 1, 1, 2, 32>>(p, x, wpk, b, dst, stream); break;
+            case 52: e = launch_geo_dtype<GeoTile<5, 2, 1, 2, 32>>(p, x, wpk, b, dst, stream); break;
+            default: e = hipErrorInvalidValue;
+        }
     } else if (p.BN == 64) {
         switch (p.KS * 10 + p.stride) {
             case 11: e = launch_geo_dtype<GeoTile<1, 1>>(p, x, wpk, b, dst, stream); break;
