@@ -130,6 +130,21 @@ def test_conv_full_size_pooled_whole_output(name):
     assert err <= TOL_BF16_ARITH
 
 
+# Layers with at most 16 or 32 output channels run the 16- and 32-channel tiles: every output
+# of a full-size layer of each against the oracle.
+@pytest.mark.parametrize("Cout,bf16", [(16, False), (32, False), (32, True)])
+def test_conv_narrow_layer_tiles_full_size_whole_output(Cout, bf16):
+    N, Cin, H, W = (16, 128, 128, 128) if bf16 else (64, 16, 224, 224)
+    x, w, b = rand_case(60 + Cout + bf16, N, Cin, H, W, Cout, bf16)
+    print(f"narrow layer ({N},{Cin},{H},{W}) -> {Cout} bf16={bf16}: running GPU", flush=True)
+    got = run_conv(x, w, b, fc.ACT_GELU, 1, bf16)
+    assert got.shape == (N, Cout) and np.all(np.isfinite(got))
+    ref = oracle.conv_act_pool(x, w, b, fc.ACT_GELU, 1)
+    err = max_rel_err(got, ref)
+    print(f"narrow layer -> {Cout}: all {got.size} outputs, err={err:.3e}", flush=True)
+    assert err <= TOL_BF16_ARITH
+
+
 def test_conv_full_size_mish2_full_output_whole():
     # every one of the 147.9 M outputs of the (32, 128, 190, 190) map, one image at a time
     name = "conv_mish2_full_f32"

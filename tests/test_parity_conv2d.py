@@ -126,6 +126,25 @@ def test_conv2d_full_size_1x1_full_output_whole():
     print(f"{name}: all {out.numel()} outputs, err={worst:.3e}", flush=True)
 
 
+# Layers with at most 32 output channels run the general kernel's 32-channel tile: every
+# output of full-size 5x5 (pooled) and 1x1 (full map) layers against the oracle.
+def test_conv2d_narrow_layer_tile_full_size_whole_output():
+    x, w, b = rand_case(70, 64, 16, 112, 112, 16, 5)
+    print("narrow 5x5 layer: running GPU", flush=True)
+    got = run_conv2d(x, w, b, 1, 2, fc.ACT_GELU, 1, False)
+    assert got.shape == (64, 16) and np.all(np.isfinite(got))
+    err = max_rel_err(got, oracle.conv2d_act_pool(x, w, b, 1, 2, fc.ACT_GELU, 1))
+    print(f"narrow 5x5 layer: all {got.size} outputs, err={err:.3e}", flush=True)
+    assert err <= TOL_F32
+    x, w, b = rand_case(71, 8, 64, 192, 192, 32, 1)
+    print("narrow 1x1 layer: running GPU", flush=True)
+    got = run_conv2d(x, w, b, 1, 0, fc.ACT_MISH2, 0, False)
+    assert got.shape == (8, 32, 192, 192) and np.all(np.isfinite(got))
+    err = max_rel_err(got, oracle.conv2d_act_pool(x, w, b, 1, 0, fc.ACT_MISH2, 0))
+    print(f"narrow 1x1 layer: all {got.size} outputs, err={err:.3e}", flush=True)
+    assert err <= TOL_F32
+
+
 def _random_case(rng):
     K = int(rng.choice([1, 3, 5]))
     S = int(rng.choice([1, 2]))
