@@ -49,7 +49,9 @@ _CSRC = "gemm_activation_reduction_amd/csrc/"
 KERNEL_SOURCES = {
     "conv3x3_fused": [_CSRC + "conv3x3.hip", _CSRC + "conv_common.h", _CSRC + "device_math.h"],
     "conv3x3_wide_bf16": [_CSRC + "conv3x3.hip", _CSRC + "conv_common.h", _CSRC + "device_math.h"],
-    "conv_general_fused": [_CSRC + "conv_general.hip", _CSRC + "conv_common.h", _CSRC + "device_math.h"],
+    "conv_general_fused": [_CSRC + "conv_general.hip", _CSRC + "conv_general_kernel.h", _CSRC + "conv_general_k1.hip",
+                           _CSRC + "conv_general_k3.hip", _CSRC + "conv_general_k5.hip", _CSRC + "conv_common.h",
+                           _CSRC + "device_math.h"],
     "gemm_lse_partials": [_CSRC + "gemm_lse.hip", _CSRC + "device_math.h"],
     "act_pool_map": [_CSRC + "epilogue.hip", _CSRC + "device_math.h"],
     "act_elementwise": [_CSRC + "epilogue.hip", _CSRC + "device_math.h"],

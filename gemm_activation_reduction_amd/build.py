@@ -10,7 +10,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libfconv.so")
-SOURCES = ["capi.hip", "conv3x3.hip", "conv_general.hip", "gemm_lse.hip", "epilogue.hip", "probe.hip"]
+SOURCES = ["capi.hip", "conv3x3.hip", "conv_general.hip", "conv_general_k1.hip", "conv_general_k3.hip",
+           "conv_general_k5.hip", "gemm_lse.hip", "epilogue.hip", "probe.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

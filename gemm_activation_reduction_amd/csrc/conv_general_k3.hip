@@ -1,0 +1,23 @@
+// Instantiations of the general-geometry convolution for 3x3 kernels (see
+// conv_general_kernel.h).
+#include "conv_general_kernel.h"
+
+namespace fconv {
+
+hipError_t launch_geo_k3(const ConvPlan& p, const void* x, const void* wpk, const float* b, float* dst,
+                         hipStream_t stream) {
+    if (p.KS != 3 || (p.stride != 1 && p.stride != 2)) return hipErrorInvalidValue;
+    const bool s1 = p.stride == 1;
+    if (p.BN == 128 && p.bf16)
+        return s1 ? launch_geo_act<true, GeoTile<3, 1, 2>>(p, x, wpk, b, dst, stream)
+                  : launch_geo_act<true, GeoTile<3, 2, 2>>(p, x, wpk, b, dst, stream);
+    if (p.BN == 32)
+        return s1 ? launch_geo_dtype<GeoTile<3, 1, 1, 2, 32>>(p, x, wpk, b, dst, stream)
+                  : launch_geo_dtype<GeoTile<3, 2, 1, 2, 32>>(p, x, wpk, b, dst, stream);
+    if (p.BN == 64)
+        return s1 ? launch_geo_dtype<GeoTile<3, 1>>(p, x, wpk, b, dst, stream)
+                  : launch_geo_dtype<GeoTile<3, 2>>(p, x, wpk, b, dst, stream);
+    return hipErrorInvalidValue;
+}
+
+}  // namespace fconv
