@@ -20,7 +20,7 @@ ConvPlan plan_conv_general(bool bf16, int act, int pool, int N, int Cin, int H, 
     p.OW = (W + 2 * pad - K) / stride + 1;
     p.TH = 8; p.TW = 32;
     // 128 channels per workgroup (8 waves) where the halo traffic per MFMA is the limit
-    p.BN = (bf16 || K == 1) && Cout >= 128 ? 128 : Cout <= 32 ? 32 : 64;
+    p.BN = (bf16 || K == 1) && Cout >= 128 ? 128 : Cout <= 16 ? 16 : Cout <= 32 ? 32 : 64;
     p.CK = bf16 ? Elem<true>::CK : Elem<false>::CK;
     p.tilesH = (p.OH + p.TH - 1) / p.TH;
     p.tilesW = (p.OW + p.TW - 1) / p.TW;

@@ -14,6 +14,9 @@ hipError_t launch_geo_k1(const ConvPlan& p, const void* x, const void* wpk, cons
     if (p.BN == 128)
         return s1 ? launch_geo_act<false, GeoTile<1, 1, 2>>(p, x, wpk, b, dst, stream)
                   : launch_geo_act<false, GeoTile<1, 2, 2>>(p, x, wpk, b, dst, stream);
+    if (p.BN == 16)
+        return s1 ? launch_geo_dtype<GeoTile<1, 1, 1, 2, 16>>(p, x, wpk, b, dst, stream)
+                  : launch_geo_dtype<GeoTile<1, 2, 1, 2, 16>>(p, x, wpk, b, dst, stream);
     if (p.BN == 32)
         return s1 ? launch_geo_dtype<GeoTile<1, 1, 1, 2, 32>>(p, x, wpk, b, dst, stream)
                   : launch_geo_dtype<GeoTile<1, 2, 1, 2, 32>>(p, x, wpk, b, dst, stream);

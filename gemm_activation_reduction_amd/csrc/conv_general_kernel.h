@@ -55,10 +55,10 @@ constexpr int kGRow = 80;  // bytes per LDS row: 64 bytes of channel data + 16 o
 
 // WO = 1: 64 output channels per workgroup, 4 waves. WO = 2: 128 output channels, 8 waves
 // (4 pixel groups x 2 channel halves): the staged halo of a step feeds twice the MFMAs, so
-// the halo bytes moved through the vector memory path per MFMA halve. BN_ = 32 (with WO = 1)
-// is the tile of layers with at most 32 output channels: 4 waves of 4 pixel blocks x 2 oc
-// blocks, so a narrow layer does not spend MFMA work and weight staging on 32 padding
-// channels.
+// the halo bytes moved through the vector memory path per MFMA halve. BN_ = 16 or 32 (with
+// WO = 1) is the tile of layers with at most 16 or 32 output channels: 4 waves of 4 pixel
+// blocks x 1 or 2 oc blocks, so a narrow layer does not spend MFMA work and weight staging
+// on padding channels.
 template <int KS_, int S_, int WO_ = 1, int OCC_ = 2, int BN_ = 64 * WO_>
 struct GeoTile {
     static constexpr int KS = KS_, S = S_, WO = WO_;
@@ -553,7 +553,7 @@ hipError_t launch_geo_dtype(const ConvPlan& p, const void* x, const void* wpk, c
 
 }  // namespace
 
-// One kernel size per translation unit: BN 32, 64 or 128 (the plan decides), stride 1 or 2,
+// One kernel size per translation unit: BN 16, 32, 64 or 128 (the plan decides), stride 1 or 2,
 // either dtype. Return hipErrorInvalidValue for a plan they do not cover.
 hipError_t launch_geo_k1(const ConvPlan& p, const void* x, const void* wpk, const float* b, float* dst,
                          hipStream_t stream);
