@@ -262,16 +262,45 @@ struct WeightStage {
 };
 
 
-template <bool BF16, bool VEC, int ACT, bool POOL, class TL>
+// fp32 layers of a single K chunk (Cin <= 16) with 16-byte halo runs stage by LDS DMA
+// (buffer_load ... lds) instead of through registers: fp32 MFMA and VALU work serialize on a
+// SIMD, and the register path spends VALU instructions on load addresses, the halo transpose
+// and LDS store addresses. The halo stays in NCHW order. Channel c occupies a 2 KB block at
+// c * 2048 + ((c >> 2) & 3) * 64 bytes: rows 0-5 in its first kilobyte and rows 6-9 in its
+// second, each row 10 slots of 16 bytes (40 pixels). One DMA instruction fills one such
+// kilobyte in lane order, lane l taking row l / 10, run l % 10 (lanes past the rows read
+// zero), so a lane's part of every load address is fixed and only the channel and the row
+// group change per instruction (wave-uniform, scalar arithmetic). The 16 x 4 lanes of an
+// fp32 fragment read (channel 4g + s for lane group g, 16 consecutive pixels) land on 64
+// distinct banks: the skew puts the four groups 16 banks apart. The weights arrive as 64-byte
+// rows (tap, oc) with K group s of row r in 16-byte slot s ^ ((r >> 1) & 3), the layout the
+// LDS-DMA GEMM reads conflict-free.
+template <class TL>
+struct DmaLayout {
+    static constexpr int RG = 6;                        // halo rows per DMA instruction
+    static constexpr int HALO_INS = 16 * 2;             // (channel, row group) pairs
+    static constexpr int HALO_BYTES = 16 * 2048 + 3 * 64 + 64;
+    static constexpr int W_ROWS = 9 * TL::BN;
+    static constexpr int W_INS = (W_ROWS / 16 + (TL::NT / 64) - 1) / (TL::NT / 64) * (TL::NT / 64);
+    static constexpr int LDS = HALO_BYTES + W_INS * 1024;
+    static_assert(TL::HR <= 2 * RG && TL::HC <= 40, "the halo fits two 6-row groups of 40 pixels");
+    static_assert(HALO_INS % (TL::NT / 64) == 0, "whole DMA instructions per wave");
+    static_assert(W_ROWS % 16 == 0, "whole 16-row weight blocks");
+    // byte offset of halo row r (0 <= r < 12) inside a channel block
+    __device__ __forceinline__ static int row_off(int r) { return r < RG ? r * 160 : 1024 + (r - RG) * 160; }
+};
+
+template <bool BF16, bool VEC, int ACT, bool POOL, class TL, bool DMA = false>
 __global__ __launch_bounds__(TL::NT) __attribute__((amdgpu_waves_per_eu(TL::MINW))) void conv3x3_fused(
     const typename Elem<BF16>::T* __restrict__ x, const typename Elem<BF16>::T* __restrict__ wp,
     const float* __restrict__ bias, float* __restrict__ dst, int Cin, int H, int W, int Cout,
     int CoutPad, int nChunk, int tilesH, int tilesW, int ocTiles, int out_align) {
     using T = typename Elem<BF16>::T;
     constexpr int CK = Elem<BF16>::CK;
-    __shared__ __attribute__((aligned(16))) unsigned char smem[TL::LDS];
+    static_assert(!DMA || (!BF16 && VEC), "DMA staging: fp32 with 16-byte halo runs");
+    __shared__ __attribute__((aligned(1024))) unsigned char smem[DMA ? DmaLayout<TL>::LDS : TL::LDS];
     unsigned char* halo = smem;
-    unsigned char* wl = smem + TL::HPOS * kRow;
+    unsigned char* wl = smem + (DMA ? DmaLayout<TL>::HALO_BYTES : TL::HPOS * kRow);
 
     int bid = xcd_contiguous_index(blockIdx.x, gridDim.x);
     const int ot = bid % ocTiles; bid /= ocTiles;
@@ -324,6 +353,14 @@ __global__ __launch_bounds__(TL::NT) __attribute__((amdgpu_waves_per_eu(TL::MINW
             for (int j = 0; j < TL::WPB; ++j) {
                 if constexpr (BF16) {
                     a[j] = *(const u4*)(a_base + ((j / TL::CB + kh) * TL::HP + (j % TL::CB) * 16 + kw) * kRow);
+                } else if constexpr (DMA) {
+                    // channel 4g + s of pixel (row + kh, col + i + kw), s = 0..3: channel block
+                    // (4g + s) * 2048 + g * 64, then the row, then the pixel
+                    const int pb = wpi * TL::WPB + j;
+                    const unsigned char* q = halo + g * (4 * 2048 + 64) + DmaLayout<TL>::row_off(pb_row(pb) + kh) +
+                                             (pb_col(pb) * 16 + i + kw) * 4;
+#pragma unroll
+                    for (int s4 = 0; s4 < 4; ++s4) a[j][s4] = *(const unsigned*)(q + s4 * 2048);
                 } else {
                     const int pb = wpi * TL::WPB + j;
                     const int pos = (pb_row(pb) + kh) * TL::HP + pb_col(pb) * 16 + i + kw;
@@ -333,7 +370,10 @@ __global__ __launch_bounds__(TL::NT) __attribute__((amdgpu_waves_per_eu(TL::MINW
     #pragma unroll
             for (int j = 0; j < TL::WOB; ++j) {
                 const int o = (woi * TL::WOB + j) * 16 + i;
-                b[j] = *(const u4*)(wl + (tap * TL::BN + o) * kRow + g * 16);
+                if constexpr (DMA)
+                    b[j] = *(const u4*)(wl + (tap * TL::BN + o) * 64 + 16 * (g ^ ((i >> 1) & 3)));
+                else
+                    b[j] = *(const u4*)(wl + (tap * TL::BN + o) * kRow + g * 16);
             }
             if constexpr (!BF16) {
     #pragma unroll
@@ -356,6 +396,48 @@ __global__ __launch_bounds__(TL::NT) __attribute__((amdgpu_waves_per_eu(TL::MINW
         }
     };
 
+    if constexpr (DMA) {
+        // nChunk == 1: the halo and the weights of the only chunk, then the MFMA work
+        typedef __attribute__((address_space(3))) void lds_t;
+        using DL = DmaLayout<TL>;
+        constexpr int NW = TL::NT / 64;
+        const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+        // Halo. Lane l: halo row (row group) * 6 + l / 10, pixels ow0 + 4 (l % 10) .. + 3. The lane's
+        // offset and its bounds test for each row group are computed once; the channel and row
+        // group of an instruction are wave-uniform and go through scalar registers.
+        const int lr = lane / 10, lrun = lane - 10 * (lane / 10);
+        const int lane_off = (lr * W + 4 * lrun) * 4;
+        const bool lane_ok = lr < DL::RG && ow0 + 4 * lrun < W;
+        const bool row_ok0 = lane_ok && lr < TL::HR && oh0 + lr < H;
+        const bool row_ok1 = lane_ok && DL::RG + lr < TL::HR && oh0 + DL::RG + lr < H;
+#pragma unroll
+        for (int k = 0; k < DL::HALO_INS / NW; ++k) {
+            const int ins = wave_u + NW * k;
+            const int c = ins >> 1, rg = ins & 1;  // wave-uniform
+            const int ubase = __builtin_amdgcn_readfirstlane(((c * H + oh0 + rg * DL::RG) * W + ow0) * 4);
+            const bool in = c < Cin && (rg ? row_ok1 : row_ok0);
+            const int off = in ? ubase + lane_off : kOOB;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (lds_t*)(halo + c * 2048 + ((c >> 2) & 3) * 64 + rg * 1024), 16,
+                                                     off, 0, 0, 0);
+        }
+        // Weights. Instruction ins fills rows 16 ins .. 16 ins + 15 of [tap][BN]: since BN is a
+        // multiple of 16 the tap and the first oc are wave-uniform; lane l takes row 16 ins + l / 4
+        // and 16-byte slot l % 4, which holds K group (l % 4) ^ ((l / 4 >> 1) & 3).
+        const int w_lane = ((lane >> 2) * 4 + ((lane & 3) ^ ((lane >> 3) & 3))) * 16;
+#pragma unroll
+        for (int k = 0; k < DL::W_INS / NW; ++k) {
+            const int ins = wave_u + NW * k;
+            const int tap = (ins * 16) / TL::BN, o0 = (ins * 16) % TL::BN;  // wave-uniform
+            const int ubase = __builtin_amdgcn_readfirstlane((tap * CoutPad + oc0 + o0) * 64);
+            const int off = ins * 16 < DL::W_ROWS ? ubase + w_lane : kOOB;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, (lds_t*)(wl + ins * 1024), 16, off, 0, 0, 0);
+        }
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0): this wave's DMA has landed
+        __builtin_amdgcn_s_barrier();        // ... and every wave's
+        asm volatile("" ::: "memory");
+        compute_chunk();
+    } else {
     using Halo = typename std::conditional<VEC, HaloVec<BF16, TL>, HaloScalar<BF16, TL>>::type;
     WeightStage<BF16, TL> wsg;
     // One chunk ahead: the next chunk's loads fly while this chunk computes.
@@ -378,6 +460,7 @@ __global__ __launch_bounds__(TL::NT) __attribute__((amdgpu_waves_per_eu(TL::MINW
         if constexpr (BF16) __builtin_amdgcn_s_setprio(1);
         compute_chunk();
         if constexpr (BF16) __builtin_amdgcn_s_setprio(0);
+    }
     }
 
     // Epilogue. Accumulator layout (16x16 MFMA output): lane (g, i) register r holds
@@ -788,6 +871,8 @@ hipError_t launch_typed(const ConvPlan& p, const void* x, const void* wpk, const
     const int vw = 16 / (int)sizeof(T);
     const bool vec = p.W % vw == 0 && (uintptr_t)x % 16 == 0;
     auto kern = vec ? conv3x3_fused<BF16, true, ACT, POOL, TL> : conv3x3_fused<BF16, false, ACT, POOL, TL>;
+    if constexpr (!BF16)
+        if (vec && p.nChunk == 1) kern = conv3x3_fused<false, true, ACT, POOL, TL, true>;
     hipLaunchKernelGGL(kern, dim3((unsigned)p.grid()), dim3(TL::NT), 0,
                        stream, (const T*)x, (const T*)wpk, b, dst, p.Cin, p.H, p.W, p.Cout, p.CoutPad,
                        p.nChunk, p.tilesH, p.tilesW, p.ocTiles,
