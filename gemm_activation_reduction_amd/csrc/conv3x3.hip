@@ -262,7 +262,7 @@ struct WeightStage {
 };
 
 
-// fp32 layers of a single K chunk (Cin <= 16) with 16-byte halo runs stage by LDS DMA
+// fp32 layers with 16-byte halo runs (W % 4 == 0) stage each K chunk by LDS DMA
 // (buffer_load ... lds) instead of through registers: fp32 MFMA and VALU work serialize on a
 // SIMD, and the register path spends VALU instructions on load addresses, the halo transpose
 // and LDS store addresses. The halo stays in NCHW order. Channel c occupies a 2 KB block at
@@ -290,7 +290,7 @@ struct DmaLayout {
     __device__ __forceinline__ static int row_off(int r) { return r < RG ? r * 160 : 1024 + (r - RG) * 160; }
 };
 
-template <bool BF16, bool VEC, int ACT, bool POOL, class TL, bool DMA = false>
+template <bool BF16, bool VEC, int ACT, bool POOL, class TL, int DMA = 0>
 __global__ __launch_bounds__(TL::NT) __attribute__((amdgpu_waves_per_eu(TL::MINW))) void conv3x3_fused(
     const typename Elem<BF16>::T* __restrict__ x, const typename Elem<BF16>::T* __restrict__ wp,
     const float* __restrict__ bias, float* __restrict__ dst, int Cin, int H, int W, int Cout,
@@ -397,7 +397,6 @@ __global__ __launch_bounds__(TL::NT) __attribute__((amdgpu_waves_per_eu(TL::MINW
     };
 
     if constexpr (DMA) {
-        // nChunk == 1: the halo and the weights of the only chunk, then the MFMA work
         typedef __attribute__((address_space(3))) void lds_t;
         using DL = DmaLayout<TL>;
         constexpr int NW = TL::NT / 64;
@@ -410,33 +409,74 @@ __global__ __launch_bounds__(TL::NT) __attribute__((amdgpu_waves_per_eu(TL::MINW
         const bool lane_ok = lr < DL::RG && ow0 + 4 * lrun < W;
         const bool row_ok0 = lane_ok && lr < TL::HR && oh0 + lr < H;
         const bool row_ok1 = lane_ok && DL::RG + lr < TL::HR && oh0 + DL::RG + lr < H;
+        if constexpr (DMA == 1) {  // the only chunk: its halo and weights, then the MFMA work
 #pragma unroll
-        for (int k = 0; k < DL::HALO_INS / NW; ++k) {
-            const int ins = wave_u + NW * k;
-            const int c = ins >> 1, rg = ins & 1;  // wave-uniform
-            const int ubase = __builtin_amdgcn_readfirstlane(((c * H + oh0 + rg * DL::RG) * W + ow0) * 4);
-            const bool in = c < Cin && (rg ? row_ok1 : row_ok0);
-            const int off = in ? ubase + lane_off : kOOB;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (lds_t*)(halo + c * 2048 + ((c >> 2) & 3) * 64 + rg * 1024), 16,
-                                                     off, 0, 0, 0);
-        }
-        // Weights. Instruction ins fills rows 16 ins .. 16 ins + 15 of [tap][BN]: since BN is a
-        // multiple of 16 the tap and the first oc are wave-uniform; lane l takes row 16 ins + l / 4
-        // and 16-byte slot l % 4, which holds K group (l % 4) ^ ((l / 4 >> 1) & 3).
-        const int w_lane = ((lane >> 2) * 4 + ((lane & 3) ^ ((lane >> 3) & 3))) * 16;
+            for (int k = 0; k < DL::HALO_INS / NW; ++k) {
+                const int ins = wave_u + NW * k;
+                const int c = ins >> 1, rg = ins & 1;  // wave-uniform
+                // unsigned: a channel past Cin (kOOB below) may lie past 2^31 bytes
+                const int ubase = (int)__builtin_amdgcn_readfirstlane((((unsigned)c * H + oh0 + rg * DL::RG) * W + ow0) * 4u);
+                const bool in = c < Cin && (rg ? row_ok1 : row_ok0);
+                const int off = in ? ubase + lane_off : kOOB;
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (lds_t*)(halo + c * 2048 + ((c >> 2) & 3) * 64 + rg * 1024), 16,
+                                                         off, 0, 0, 0);
+            }
+            // Weights. Instruction ins fills rows 16 ins .. 16 ins + 15 of [tap][BN]: since BN is a
+            // multiple of 16 the tap and the first oc are wave-uniform; lane l takes row 16 ins + l / 4
+            // and 16-byte slot l % 4, which holds K group (l % 4) ^ ((l / 4 >> 1) & 3).
+            const int w_lane = ((lane >> 2) * 4 + ((lane & 3) ^ ((lane >> 3) & 3))) * 16;
 #pragma unroll
-        for (int k = 0; k < DL::W_INS / NW; ++k) {
-            const int ins = wave_u + NW * k;
-            const int tap = (ins * 16) / TL::BN, o0 = (ins * 16) % TL::BN;  // wave-uniform
-            const int ubase = __builtin_amdgcn_readfirstlane((tap * CoutPad + oc0 + o0) * 64);
-            const int off = ins * 16 < DL::W_ROWS ? ubase + w_lane : kOOB;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, (lds_t*)(wl + ins * 1024), 16, off, 0, 0, 0);
+            for (int k = 0; k < DL::W_INS / NW; ++k) {
+                const int ins = wave_u + NW * k;
+                const int tap = (ins * 16) / TL::BN, o0 = (ins * 16) % TL::BN;  // wave-uniform
+                const int ubase = __builtin_amdgcn_readfirstlane((tap * CoutPad + oc0 + o0) * 64);
+                const int off = ins * 16 < DL::W_ROWS ? ubase + w_lane : kOOB;
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, (lds_t*)(wl + ins * 1024), 16, off, 0, 0, 0);
+            }
+            asm volatile("" ::: "memory");
+            __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0): this wave's DMA has landed
+            __builtin_amdgcn_s_barrier();        // ... and every wave's
+            asm volatile("" ::: "memory");
+            compute_chunk();
+        } else {  // the same staging for chunk after chunk, in one LDS buffer
+            // One chunk at a time: the co-resident workgroup's MFMA work covers this one's DMA
+            // latency (the register path overlaps it inside the workgroup instead).
+            const int w_lane = ((lane >> 2) * 4 + ((lane & 3) ^ ((lane >> 3) & 3))) * 16;
+            for (int ch = 0; ch < nChunk; ++ch) {
+                const int c0 = ch * CK;
+                if (ch) {  // every wave is done reading the previous chunk
+                    asm volatile("" ::: "memory");
+                    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+                    __builtin_amdgcn_s_barrier();
+                    asm volatile("" ::: "memory");
+                }
+#pragma unroll
+                for (int k = 0; k < DL::HALO_INS / NW; ++k) {
+                    const int ins = wave_u + NW * k;
+                    const int c = ins >> 1, rg = ins & 1;
+                    // unsigned: a channel past Cin (kOOB below) may lie past 2^31 bytes
+                    const int ubase = (int)__builtin_amdgcn_readfirstlane(
+                        (((unsigned)(c0 + c) * H + oh0 + rg * DL::RG) * W + ow0) * 4u);
+                    const bool in = c0 + c < Cin && (rg ? row_ok1 : row_ok0);
+                    const int off = in ? ubase + lane_off : kOOB;
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                        xr, (lds_t*)(halo + c * 2048 + ((c >> 2) & 3) * 64 + rg * 1024), 16, off, 0, 0, 0);
+                }
+#pragma unroll
+                for (int k = 0; k < DL::W_INS / NW; ++k) {
+                    const int ins = wave_u + NW * k;
+                    const int tap = (ins * 16) / TL::BN, o0 = (ins * 16) % TL::BN;
+                    const int ubase = __builtin_amdgcn_readfirstlane(((ch * 9 + tap) * CoutPad + oc0 + o0) * 64);
+                    const int off = ins * 16 < DL::W_ROWS ? ubase + w_lane : kOOB;
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, (lds_t*)(wl + ins * 1024), 16, off, 0, 0, 0);
+                }
+                asm volatile("" ::: "memory");
+                __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0)
+                __builtin_amdgcn_s_barrier();
+                asm volatile("" ::: "memory");
+                compute_chunk();
+            }
         }
-        asm volatile("" ::: "memory");
-        __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0): this wave's DMA has landed
-        __builtin_amdgcn_s_barrier();        // ... and every wave's
-        asm volatile("" ::: "memory");
-        compute_chunk();
     } else {
     using Halo = typename std::conditional<VEC, HaloVec<BF16, TL>, HaloScalar<BF16, TL>>::type;
     WeightStage<BF16, TL> wsg;
@@ -872,7 +912,7 @@ hipError_t launch_typed(const ConvPlan& p, const void* x, const void* wpk, const
     const bool vec = p.W % vw == 0 && (uintptr_t)x % 16 == 0;
     auto kern = vec ? conv3x3_fused<BF16, true, ACT, POOL, TL> : conv3x3_fused<BF16, false, ACT, POOL, TL>;
     if constexpr (!BF16)
-        if (vec && p.nChunk == 1) kern = conv3x3_fused<false, true, ACT, POOL, TL, true>;
+        if (vec) kern = p.nChunk == 1 ? conv3x3_fused<false, true, ACT, POOL, TL, 1> : conv3x3_fused<false, true, ACT, POOL, TL, 2>;
     hipLaunchKernelGGL(kern, dim3((unsigned)p.grid()), dim3(TL::NT), 0,
                        stream, (const T*)x, (const T*)wpk, b, dst, p.Cin, p.H, p.W, p.Cout, p.CoutPad,
                        p.nChunk, p.tilesH, p.tilesW, p.ocTiles,

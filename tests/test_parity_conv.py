@@ -42,10 +42,12 @@ SHAPES = [
     (1, 16, 36, 34, 64),   # OW = 32: exactly one tile column, OW % 4 == 0
     (1, 7, 3, 70, 5),      # a single output row
     (2, 33, 20, 21, 16),   # Cin one past a bf16 chunk, odd OW
-    # fp32 with Cin <= 16 and W % 4 == 0 stages by LDS DMA: its edges
+    # fp32 with W % 4 == 0 stages by LDS DMA: its edges
     (2, 5, 19, 20, 7),     # W a multiple of 4 but not 8, ragged rows and columns
     (1, 16, 11, 36, 33),   # OW = 34: a second tile column holding two pixels
     (3, 1, 3, 12, 64),     # a single output row, one input channel
+    (1, 40, 13, 28, 20),   # three chunks, the last holding 8 channels
+    (2, 64, 9, 44, 96),    # four full chunks, a second oc tile of 32 channels
 ]
 
 

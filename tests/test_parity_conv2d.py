@@ -174,4 +174,3 @@ def test_conv2d_random_shapes(seed):
     print(f"  err={err:.3e}", flush=True)
     assert err <= (TOL_BF16 if bf16 else TOL_F32)
     assert err <= TOL_BF16_ARITH
-    assert err <= TOL_BF16_ARITH
