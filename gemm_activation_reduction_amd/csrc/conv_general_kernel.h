@@ -26,6 +26,9 @@
 // output columns of a fragment read 16 consecutive LDS rows for every tap -- the same
 // conflict-free pattern as stride 1.
 //
+// fp32 1x1 stride-1 layers of 128 or more output channels with 16-byte halo runs stage
+// each chunk by LDS DMA into a double buffer instead (GeoDma below).
+//
 // Halo loads: when W is a whole number of 16-byte pixel groups and x is 16-byte aligned,
 // 16-byte runs along W (ow0 S is a multiple of 32, so the misalignment (-P) mod run is
 // the same for every tile and every aligned run lies wholly inside or wholly outside the
@@ -273,14 +276,38 @@ struct GeoWeights {
     }
 };
 
-template <bool BF16, bool VEC, int ACT, bool POOL, class TL>
+// fp32 1x1 stride-1 layers with 16-byte halo runs stage each chunk by LDS DMA (buffer_load
+// ... lds) into one of two buffers, the next chunk's DMA flying while this chunk computes. fp32
+// MFMA and VALU work serialize on a SIMD, and the register path spends VALU instructions on
+// load addresses, the transpose to channel-minor rows and the LDS stores. The halo stays in
+// NCHW order: channel c owns 1 KB at c * 1024 + ((c >> 2) & 3) * 64, its 8 tile rows of 32
+// pixels 128 bytes apart. One DMA instruction fills one channel in lane order (lane l: row
+// l / 8, 4-pixel run l % 8), so the channel is the only per-instruction part of an address.
+// An fp32 fragment (channel 4g + s for lane group g, 16 consecutive pixels) is one
+// ds_read_b32 per lane on 64 distinct banks: the skew puts the four groups 16 banks apart.
+// The weights arrive as 64-byte rows with K group s of row r in 16-byte slot s ^ ((r >> 1) &
+// 3), the layout the LDS-DMA GEMM reads conflict-free.
+template <class TL>
+struct GeoDma {
+    static constexpr int NW = TL::NT / 64;
+    static constexpr int HALO_INS = 16;  // one per channel of a chunk
+    static constexpr int HALO_BYTES = 16 * 1024 + 256;
+    static constexpr int W_INS = (TL::BN / 16 + NW - 1) / NW * NW;  // 16 weight rows each
+    static constexpr int BUF = HALO_BYTES + W_INS * 1024;
+    static constexpr int LDS = 2 * BUF;
+};
+
+template <bool BF16, bool VEC, int ACT, bool POOL, class TL, bool DMA = false>
 __global__ __launch_bounds__(TL::NT) __attribute__((amdgpu_waves_per_eu(TL::OCC))) void conv_general_fused(
     const typename Elem<BF16>::T* __restrict__ x, const typename Elem<BF16>::T* __restrict__ wp,
     const float* __restrict__ bias, float* __restrict__ dst, int Cin, int H, int W, int Cout, int OH, int OW,
     int pad, int CoutPad, int nChunk, int tilesH, int tilesW, int ocTiles, int out_align) {
     using T = typename Elem<BF16>::T;
     constexpr int KS = TL::KS, S = TL::S;
-    __shared__ __attribute__((aligned(16))) unsigned char smem[TL::LDS];
+    static_assert(!DMA || (!BF16 && VEC && KS == 1 && S == 1 && TL::TH == 8 && TL::TW == 32),
+                  "DMA staging: fp32 1x1 stride-1 8 x 32 tiles with 16-byte halo runs");
+    static_assert(!DMA || GeoDma<TL>::HALO_INS % GeoDma<TL>::NW == 0, "whole DMA instructions per wave");
+    __shared__ __attribute__((aligned(16))) unsigned char smem[DMA ? GeoDma<TL>::LDS : TL::LDS];
     unsigned char* halo = smem;
     unsigned char* wl = smem + TL::HPOS * kGRow;
 
@@ -361,66 +388,140 @@ __global__ __launch_bounds__(TL::NT) __attribute__((amdgpu_waves_per_eu(TL::OCC)
         }
     };
 
-    // Steps (chunk c, kernel row kh), kh fastest; the next step's loads fly while this
-    // step computes.
-    const int nStep = nChunk * KS;
-    using Halo = typename std::conditional<VEC, GeoHaloVec<BF16, TL>, GeoHalo<BF16, TL>>::type;
-    Halo hs;
-    GeoWeights<BF16, TL> wsg;
-    constexpr int CK = Elem<BF16>::CK;
-    constexpr int VW = 16 / (int)sizeof(T);
-    const int mis = ((-pad) % VW + VW) % VW;  // iw0 - mis is a multiple of VW
-    const int hcol0 = VEC ? iw0 - mis : iw0;
-    auto halo_store = [&]() {
-        if constexpr (VEC) hs.store(halo, mis, tid);
-        else hs.store(halo, tid);
-    };
-    hs.setup(H, W, hcol0, tid);
-    const bool last_used = Halo::last_used(tid);
-    hs.load(xr, H, W, Cin, 0, oh0 * S - pad, hcol0, tid);
-    wsg.load(wr, CoutPad, 0, oc0, tid);
-    // The next step's loads are spread between this step's MFMAs instead of issued as one
-    // burst: the texture unit takes a 16-byte-per-lane load every ~16 cycles, so a burst from
-    // every wave stalled each wave ~1.5-2.3 k cycles in issue before its first MFMA.
-    constexpr int kMfmaPerStep = KS * TL::WPB * TL::WOB * (BF16 ? 1 : 4);
-    constexpr int kLoadsPerStep = Halo::PER * Elem<BF16>::EPG + GeoWeights<BF16, TL>::PER;
-    constexpr int kMfmaPerLoad = kMfmaPerStep / kLoadsPerStep > 0 ? kMfmaPerStep / kLoadsPerStep : 1;
-    // Only the 8-wave bf16 tile with 16-byte runs and K < 5: elsewhere it made the compiler spill.
-    constexpr bool kInterleave = BF16 && VEC && TL::WO == 2 && KS < 5;
-    for (int st = 0; st < nStep; ++st) {
-        if (st) __syncthreads();  // every wave is done reading the previous step
-        halo_store();
-        wsg.store(wl, tid);
-        __syncthreads();
-        if constexpr (kInterleave) {
-            if (st + 1 < nStep) {
-                const int c = (st + 1) / KS, kh = (st + 1) % KS;
-                // loads and MFMAs in one basic block, so the scheduler can interleave them; a
-                // wave with no halo item in its last round leaves those loads out
-                auto load_and_compute = [&](auto with_last) {
-                    hs.template load<decltype(with_last)::value>(xr, H, W, Cin, c * CK, oh0 * S + kh - pad, hcol0,
-                                                                 tid);
-                    wsg.load(wr, CoutPad, (c * KS + kh) * KS, oc0, tid);
-                    compute_step();
+    if constexpr (DMA) {
+        typedef __attribute__((address_space(3))) void lds_t;
+        using DL = GeoDma<TL>;
+        constexpr int NW = DL::NW;
+        constexpr int CK = Elem<false>::CK;
+        const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+        // Halo: lane l takes row l / 8, pixels ow0 + 4 (l % 8) .. + 3; a run lies wholly inside
+        // or outside the image (W % 4 == 0), outside runs and channels past Cin read zero.
+        const int lr = lane >> 3, lrun = lane & 7;
+        const bool lane_ok = oh0 + lr < H && ow0 + 4 * lrun < W;
+        const int lane_off = (lr * W + 4 * lrun) * 4;
+        const int w_lane = ((lane >> 2) * 4 + ((lane & 3) ^ ((lane >> 3) & 3))) * 16;
+        auto stage = [&](int ch, unsigned char* buf) {
+            const int c0 = ch * CK;
 #pragma unroll
-                    for (int k = 0; k < kLoadsPerStep; ++k) {
-                        __builtin_amdgcn_sched_group_barrier(0x008, kMfmaPerLoad, 0);  // MFMA
-                        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);             // VMEM read
-                    }
-                };
-                if (last_used) load_and_compute(std::true_type{});
-                else load_and_compute(std::false_type{});
+            for (int k = 0; k < DL::HALO_INS / NW; ++k) {
+                const int c = wave_u + NW * k;  // wave-uniform
+                // unsigned: a channel past Cin (kOOB below) may lie past 2^31 bytes
+                const int ubase = (int)__builtin_amdgcn_readfirstlane((((unsigned)(c0 + c) * H + oh0) * W + ow0) * 4u);
+                const int off = c0 + c < Cin && lane_ok ? ubase + lane_off : kOOB;
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (lds_t*)(buf + c * 1024 + ((c >> 2) & 3) * 64), 16, off,
+                                                         0, 0, 0);
+            }
+            // Weights: instruction ins fills rows 16 ins .. 16 ins + 15; lane l takes row
+            // 16 ins + l / 4 and 16-byte slot l % 4, which holds K group (l % 4) ^ ((l / 4 >> 1) & 3).
+            unsigned char* wb = buf + DL::HALO_BYTES;
+#pragma unroll
+            for (int k = 0; k < DL::W_INS / NW; ++k) {
+                const int ins = wave_u + NW * k;
+                const int ubase = __builtin_amdgcn_readfirstlane((ch * CoutPad + oc0 + ins * 16) * 64);
+                const int off = ins * 16 < TL::BN ? ubase + w_lane : kOOB;
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, (lds_t*)(wb + ins * 1024), 16, off, 0, 0, 0);
+            }
+        };
+        auto compute = [&](const unsigned char* buf) {
+            const unsigned char* wb = buf + DL::HALO_BYTES;
+            u4 b[TL::WOB];
+#pragma unroll
+            for (int j = 0; j < TL::WOB; ++j) {
+                const int o = (woi * TL::WOB + j) * 16 + i;
+                b[j] = *(const u4*)(wb + o * 64 + 16 * (g ^ ((i >> 1) & 3)));
+            }
+            unsigned a[TL::WPB][4];
+#pragma unroll
+            for (int j = 0; j < TL::WPB; ++j) {
+                const int pb = wpi * TL::WPB + j;
+                const unsigned char* q =
+                    buf + g * (4 * 1024 + 64) + pb_row(pb) * 128 + (pb_col(pb) * 16 + i) * 4;
+#pragma unroll
+                for (int s4 = 0; s4 < 4; ++s4) a[j][s4] = *(const unsigned*)(q + s4 * 1024);
+            }
+#pragma unroll
+            for (int s4 = 0; s4 < 4; ++s4)
+#pragma unroll
+                for (int jp = 0; jp < TL::WPB; ++jp)
+#pragma unroll
+                    for (int jo = 0; jo < TL::WOB; ++jo)
+                        acc[jp][jo] = __builtin_amdgcn_mfma_f32_16x16x4f32(
+                            __uint_as_float(a[jp][s4]), __uint_as_float(b[jo][s4]), acc[jp][jo], 0, 0, 0);
+        };
+        // Chunk ch + 1 goes into the other buffer while chunk ch computes; one barrier per
+        // chunk both publishes the landed chunk and retires the buffer read before it.
+        stage(0, smem);
+        for (int ch = 0; ch < nChunk; ++ch) {
+            asm volatile("" ::: "memory");
+            __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0): this wave's DMA has landed
+            __builtin_amdgcn_s_barrier();        // ... and every wave's; the other buffer is free
+            asm volatile("" ::: "memory");
+            if (ch + 1 < nChunk) stage(ch + 1, smem + ((ch + 1) & 1) * DL::BUF);
+            compute(smem + (ch & 1) * DL::BUF);
+        }
+    } else {
+        // Steps (chunk c, kernel row kh), kh fastest; the next step's loads fly while this
+        // step computes.
+        const int nStep = nChunk * KS;
+        using Halo = typename std::conditional<VEC, GeoHaloVec<BF16, TL>, GeoHalo<BF16, TL>>::type;
+        Halo hs;
+        GeoWeights<BF16, TL> wsg;
+        constexpr int CK = Elem<BF16>::CK;
+        constexpr int VW = 16 / (int)sizeof(T);
+        const int mis = ((-pad) % VW + VW) % VW;  // iw0 - mis is a multiple of VW
+        const int hcol0 = VEC ? iw0 - mis : iw0;
+        auto halo_store = [&]() {
+            if constexpr (VEC) hs.store(halo, mis, tid);
+            else hs.store(halo, tid);
+        };
+        hs.setup(H, W, hcol0, tid);
+        const bool last_used = Halo::last_used(tid);
+        hs.load(xr, H, W, Cin, 0, oh0 * S - pad, hcol0, tid);
+        wsg.load(wr, CoutPad, 0, oc0, tid);
+        // The next step's loads are spread between this step's MFMAs instead of issued as one
+        // burst: the texture unit takes a 16-byte-per-lane load every ~16 cycles, so a burst from
+        // every wave stalled each wave ~1.5-2.3 k cycles in issue before its first MFMA.
+        constexpr int kMfmaPerStep = KS * TL::WPB * TL::WOB * (BF16 ? 1 : 4);
+        constexpr int kLoadsPerStep = Halo::PER * Elem<BF16>::EPG + GeoWeights<BF16, TL>::PER;
+        constexpr int kMfmaPerLoad = kMfmaPerStep / kLoadsPerStep > 0 ? kMfmaPerStep / kLoadsPerStep : 1;
+        // Only the 8-wave bf16 tile with 16-byte runs and K < 5: elsewhere it made the compiler spill.
+        constexpr bool kInterleave = BF16 && VEC && TL::WO == 2 && KS < 5;
+        for (int st = 0; st < nStep; ++st) {
+            if (st) __syncthreads();  // every wave is done reading the previous step
+            halo_store();
+            wsg.store(wl, tid);
+            __syncthreads();
+            if constexpr (kInterleave) {
+                if (st + 1 < nStep) {
+                    const int c = (st + 1) / KS, kh = (st + 1) % KS;
+                    // loads and MFMAs in one basic block, so the scheduler can interleave them; a
+                    // wave with no halo item in its last round leaves those loads out
+                    auto load_and_compute = [&](auto with_last) {
+                        hs.template load<decltype(with_last)::value>(xr, H, W, Cin, c * CK, oh0 * S + kh - pad, hcol0,
+                                                                     tid);
+                        wsg.load(wr, CoutPad, (c * KS + kh) * KS, oc0, tid);
+                        compute_step();
+#pragma unroll
+                        for (int k = 0; k < kLoadsPerStep; ++k) {
+                            __builtin_amdgcn_sched_group_barrier(0x008, kMfmaPerLoad, 0);  // MFMA
+                            __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);             // VMEM read
+                        }
+                    };
+                    if (last_used) load_and_compute(std::true_type{});
+                    else load_and_compute(std::false_type{});
+                } else {
+                    compute_step();
+                }
             } else {
+                if (st + 1 < nStep) {
+                    const int c = (st + 1) / KS, kh = (st + 1) % KS;
+                    hs.load(xr, H, W, Cin, c * CK, oh0 * S + kh - pad, hcol0, tid);
+                    wsg.load(wr, CoutPad, (c * KS + kh) * KS, oc0, tid);
+                }
                 compute_step();
             }
-        } else {
-            if (st + 1 < nStep) {
-                const int c = (st + 1) / KS, kh = (st + 1) % KS;
-                hs.load(xr, H, W, Cin, c * CK, oh0 * S + kh - pad, hcol0, tid);
-                wsg.load(wr, CoutPad, (c * KS + kh) * KS, oc0, tid);
-            }
-            compute_step();
         }
+
     }
 
     // Epilogue. Lane (g, i) register r holds pixel 4g + r of the pixel block and output
@@ -509,7 +610,9 @@ __global__ __launch_bounds__(TL::NT) __attribute__((amdgpu_waves_per_eu(TL::OCC)
     }
 }
 
-template <bool BF16, int ACT, bool POOL, class TL>
+// DMA: the caller has checked that the layer has 16-byte halo runs (W % 4 == 0, x 16-byte
+// aligned) and no padding.
+template <bool BF16, int ACT, bool POOL, class TL, bool DMA = false>
 hipError_t launch_geo_typed(const ConvPlan& p, const void* x, const void* wpk, const float* b, float* dst,
                             hipStream_t stream) {
     using T = typename Elem<BF16>::T;
@@ -519,7 +622,9 @@ hipError_t launch_geo_typed(const ConvPlan& p, const void* x, const void* wpk, c
     constexpr bool kVecOK = !(BF16 && TL::KS == 5 && TL::S == 2);
     const bool vec = kVecOK && p.W % (16 / (int)sizeof(T)) == 0 && (uintptr_t)x % 16 == 0;
     auto kern = conv_general_fused<BF16, false, ACT, POOL, TL>;
-    if constexpr (kVecOK)
+    if constexpr (DMA)
+        kern = conv_general_fused<false, true, ACT, POOL, TL, true>;
+    else if constexpr (kVecOK)
         if (vec) kern = conv_general_fused<BF16, true, ACT, POOL, TL>;
     hipLaunchKernelGGL(kern, dim3((unsigned)p.grid()), dim3(TL::NT), 0, stream,
                        (const T*)x, (const T*)wpk, b, dst, p.Cin, p.H, p.W, p.Cout, p.OH, p.OW, p.pad, p.CoutPad,
@@ -528,18 +633,18 @@ hipError_t launch_geo_typed(const ConvPlan& p, const void* x, const void* wpk, c
     return hipGetLastError();
 }
 
-template <bool BF16, class TL>
+template <bool BF16, class TL, bool DMA = false>
 hipError_t launch_geo_act(const ConvPlan& p, const void* x, const void* wpk, const float* b, float* dst,
                           hipStream_t stream) {
     switch (p.act * 2 + p.pool) {
-        case 0: return launch_geo_typed<BF16, kActNone, false, TL>(p, x, wpk, b, dst, stream);
-        case 1: return launch_geo_typed<BF16, kActNone, true, TL>(p, x, wpk, b, dst, stream);
-        case 2: return launch_geo_typed<BF16, kActGelu, false, TL>(p, x, wpk, b, dst, stream);
-        case 3: return launch_geo_typed<BF16, kActGelu, true, TL>(p, x, wpk, b, dst, stream);
-        case 4: return launch_geo_typed<BF16, kActMish2, false, TL>(p, x, wpk, b, dst, stream);
-        case 5: return launch_geo_typed<BF16, kActMish2, true, TL>(p, x, wpk, b, dst, stream);
-        case 6: return launch_geo_typed<BF16, kActGeluTanh, false, TL>(p, x, wpk, b, dst, stream);
-        case 7: return launch_geo_typed<BF16, kActGeluTanh, true, TL>(p, x, wpk, b, dst, stream);
+        case 0: return launch_geo_typed<BF16, kActNone, false, TL, DMA>(p, x, wpk, b, dst, stream);
+        case 1: return launch_geo_typed<BF16, kActNone, true, TL, DMA>(p, x, wpk, b, dst, stream);
+        case 2: return launch_geo_typed<BF16, kActGelu, false, TL, DMA>(p, x, wpk, b, dst, stream);
+        case 3: return launch_geo_typed<BF16, kActGelu, true, TL, DMA>(p, x, wpk, b, dst, stream);
+        case 4: return launch_geo_typed<BF16, kActMish2, false, TL, DMA>(p, x, wpk, b, dst, stream);
+        case 5: return launch_geo_typed<BF16, kActMish2, true, TL, DMA>(p, x, wpk, b, dst, stream);
+        case 6: return launch_geo_typed<BF16, kActGeluTanh, false, TL, DMA>(p, x, wpk, b, dst, stream);
+        case 7: return launch_geo_typed<BF16, kActGeluTanh, true, TL, DMA>(p, x, wpk, b, dst, stream);
         default: return hipErrorInvalidValue;
     }
 }
