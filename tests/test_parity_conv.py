@@ -323,6 +323,27 @@ def test_conv_wide_matches_narrow_full_map(shape):
 # bf16 pooled at the baseline workload's depth (four or more 32-channel chunks) on grids of
 # 1024 or more tiles, four or more per CU: ragged channel chunks, tile rows and columns and
 # oc tiles; tile counts that do not divide evenly among the CUs or the eight XCDs.
+# fp32 layers with W % 4 == 0 and a 16-byte aligned x stage by LDS DMA; an x 4 bytes past a
+# 16-byte boundary takes the element-wise register path. Both accumulate chunk by chunk, tap
+# by tap and channel group by channel group from the bias, so full maps and pooled outputs
+# agree bit for bit: one chunk (16-channel tile), three chunks with an 8-channel tail
+# (32-channel tile), four chunks over two oc tiles, and a larger multi-tile image.
+@pytest.mark.parametrize("shape", [(2, 5, 19, 20, 7), (1, 40, 13, 28, 20), (2, 64, 9, 44, 96), (4, 64, 66, 68, 128)])
+def test_conv_f32_dma_matches_register_path(shape):
+    x, w, b = rand_case(hash(shape) % 971 + 5, *shape)
+    xd = to_device(x)
+    flat = torch.empty(xd.numel() + 1, dtype=torch.float32, device=xd.device)
+    flat[1:] = xd.reshape(-1)
+    xu = flat[1:].view(xd.shape)
+    assert xd.data_ptr() % 16 == 0 and xu.data_ptr() % 16 != 0
+    wd, bd = to_device(w), to_device(b)
+    for act, pool in (("gelu", True), ("mish2", False), ("gelu_tanh", False)):
+        o_dma = fc.conv_act_pool(xd, wd, bd, act=act, pool=pool)
+        o_reg = fc.conv_act_pool(xu, wd, bd, act=act, pool=pool)
+        torch.cuda.synchronize()
+        assert torch.equal(o_dma, o_reg), (act, pool)
+
+
 WIDE_DEEP_SHAPES = [
     (24, 100, 37, 72, 300),   # 1296 tiles: a 4-channel tail chunk, ragged rows, columns and oc tile
     (75, 128, 30, 40, 256),   # 1050 tiles (not a multiple of 8): exactly four chunks, 7 x 2 tiles per image

@@ -145,6 +145,28 @@ def test_conv2d_narrow_layer_tile_full_size_whole_output():
     assert err <= TOL_F32
 
 
+# fp32 1x1 stride-1 layers of 128 or more output channels with W % 4 == 0 and a 16-byte aligned
+# x stage by LDS DMA; an x 4 bytes past a 16-byte boundary takes the element-wise register
+# path. Both accumulate chunk by chunk and channel group by channel group from the bias, so
+# the outputs agree bit for bit: ragged rows and columns, a 1-channel second oc tile, a
+# channel tail chunk, and a larger image.
+@pytest.mark.parametrize("shape", [(1, 64, 17, 48, 144), (2, 8, 11, 24, 129), (3, 40, 21, 36, 200),
+                                   (8, 64, 64, 64, 128)])
+def test_conv2d_1x1_f32_dma_matches_register_path(shape):
+    x, w, b = rand_case(hash(shape) % 967 + 9, *shape, 1)
+    xd = to_device(x)
+    flat = torch.empty(xd.numel() + 1, dtype=torch.float32, device=xd.device)
+    flat[1:] = xd.reshape(-1)
+    xu = flat[1:].view(xd.shape)
+    assert xd.data_ptr() % 16 == 0 and xu.data_ptr() % 16 != 0
+    wd, bd = to_device(w), to_device(b)
+    for act, pool in (("mish2", False), ("gelu", True), ("none", False)):
+        o_dma = fc.conv2d_act_pool(xd, wd, bd, stride=1, pad=0, act=act, pool=pool)
+        o_reg = fc.conv2d_act_pool(xu, wd, bd, stride=1, pad=0, act=act, pool=pool)
+        torch.cuda.synchronize()
+        assert torch.equal(o_dma, o_reg), (act, pool)
+
+
 def _random_case(rng):
     K = int(rng.choice([1, 3, 5]))
     S = int(rng.choice([1, 2]))
