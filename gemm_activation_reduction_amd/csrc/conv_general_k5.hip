@@ -11,6 +11,12 @@ hipError_t launch_geo_k5(const ConvPlan& p, const void* x, const void* wpk, cons
     if (p.BN == 128 && p.bf16)
         return s1 ? launch_geo_act<true, GeoTile<5, 1, 2>>(p, x, wpk, b, dst, stream)
                   : launch_geo_act<true, GeoTile<5, 2, 2>>(p, x, wpk, b, dst, stream);
+    // fp32 stride 1 with 16-byte halo runs: LDS-DMA staging
+    if (!p.bf16 && s1 && p.W % 4 == 0 && (uintptr_t)x % 16 == 0) {
+        if (p.BN == 16) return launch_geo_act<false, GeoTile<5, 1, 1, 2, 16>, 2>(p, x, wpk, b, dst, stream);
+        if (p.BN == 32) return launch_geo_act<false, GeoTile<5, 1, 1, 2, 32>, 2>(p, x, wpk, b, dst, stream);
+        if (p.BN == 64) return launch_geo_act<false, GeoTile<5, 1>, 2>(p, x, wpk, b, dst, stream);
+    }
     if (p.BN == 16)
         return s1 ? launch_geo_dtype<GeoTile<5, 1, 1, 2, 16>>(p, x, wpk, b, dst, stream)
                   : launch_geo_dtype<GeoTile<5, 2, 1, 2, 16>>(p, x, wpk, b, dst, stream);

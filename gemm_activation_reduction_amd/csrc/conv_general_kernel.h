@@ -27,7 +27,9 @@
 // conflict-free pattern as stride 1.
 //
 // fp32 1x1 stride-1 layers of 128 or more output channels with 16-byte halo runs stage
-// each chunk by LDS DMA into a double buffer instead (GeoDma below).
+// each chunk by LDS DMA into a double buffer instead (GeoDma below), and fp32 stride-1 3x3
+// and 5x5 layers with 16-byte halo runs stage each chunk's whole halo, and each kernel row's
+// weights, by LDS DMA (GeoDmaK below).
 //
 // Halo loads: when W is a whole number of 16-byte pixel groups and x is 16-byte aligned,
 // 16-byte runs along W (ow0 S is a multiple of 32, so the misalignment (-P) mod run is
@@ -297,17 +299,46 @@ struct GeoDma {
     static constexpr int LDS = 2 * BUF;
 };
 
-template <bool BF16, bool VEC, int ACT, bool POOL, class TL, bool DMA = false>
+// fp32 stride-1 layers with K = 3 or 5 and 16-byte halo runs stage the same way. A chunk's
+// whole halo (TH + K - 1 rows, the 40 input columns from ow0 - P rounded down to a 4-pixel run)
+// arrives once, as in the 3x3 valid kernel: channel c at c * 2048 + ((c >> 2) & 3) * 64, rows
+// 0-5 in its first kilobyte and rows 6-11 in its second (160 bytes each), one DMA instruction
+// per (channel, 6-row group) with lane l taking row l / 10, run l % 10. The weights of one
+// kernel row (K taps x BN rows of 64 bytes, swizzled as above) go into one of two buffers, the
+// next row's DMA flying while this row's K taps compute; all K^2 taps of a 64-channel tile
+// would not leave room for two workgroups per CU.
+template <class TL>
+struct GeoDmaK {
+    static constexpr int NW = TL::NT / 64;
+    static constexpr int RG = 6;                          // halo rows per DMA instruction
+    static constexpr int HR = TL::TH + TL::KS - 1;        // halo rows
+    static constexpr int HALO_INS = 16 * 2;               // (channel, row group) pairs
+    static constexpr int HALO_BYTES = 16 * 2048 + 256;
+    static constexpr int W_ROWS = TL::KS * TL::BN;        // one kernel row's weights
+    static constexpr int W_INS = (W_ROWS / 16 + NW - 1) / NW * NW;
+    static constexpr int WBUF = W_INS * 1024;
+    static constexpr int LDS = HALO_BYTES + 2 * WBUF;
+    // byte offset of halo row r (0 <= r < 12) inside a channel block
+    __device__ __forceinline__ static int row_off(int r) { return r < RG ? r * 160 : 1024 + (r - RG) * 160; }
+};
+
+// DMA: 0 = register staging, 1 = the 1x1 double-buffered DMA (GeoDma), 2 = the K x K
+// stride-1 DMA (GeoDmaK).
+template <bool BF16, bool VEC, int ACT, bool POOL, class TL, int DMA = 0>
 __global__ __launch_bounds__(TL::NT) __attribute__((amdgpu_waves_per_eu(TL::OCC))) void conv_general_fused(
     const typename Elem<BF16>::T* __restrict__ x, const typename Elem<BF16>::T* __restrict__ wp,
     const float* __restrict__ bias, float* __restrict__ dst, int Cin, int H, int W, int Cout, int OH, int OW,
     int pad, int CoutPad, int nChunk, int tilesH, int tilesW, int ocTiles, int out_align) {
     using T = typename Elem<BF16>::T;
     constexpr int KS = TL::KS, S = TL::S;
-    static_assert(!DMA || (!BF16 && VEC && KS == 1 && S == 1 && TL::TH == 8 && TL::TW == 32),
-                  "DMA staging: fp32 1x1 stride-1 8 x 32 tiles with 16-byte halo runs");
-    static_assert(!DMA || GeoDma<TL>::HALO_INS % GeoDma<TL>::NW == 0, "whole DMA instructions per wave");
-    __shared__ __attribute__((aligned(16))) unsigned char smem[DMA ? GeoDma<TL>::LDS : TL::LDS];
+    static_assert(DMA != 1 || (!BF16 && VEC && KS == 1 && S == 1 && TL::TH == 8 && TL::TW == 32),
+                  "1x1 DMA staging: fp32 1x1 stride-1 8 x 32 tiles with 16-byte halo runs");
+    static_assert(DMA != 1 || GeoDma<TL>::HALO_INS % GeoDma<TL>::NW == 0, "whole DMA instructions per wave");
+    static_assert(DMA != 2 || (!BF16 && VEC && (KS == 3 || KS == 5) && S == 1 && TL::TH == 8 && TL::TW == 32),
+                  "K x K DMA staging: fp32 stride-1 8 x 32 tiles with 16-byte halo runs");
+    static_assert(DMA != 2 || GeoDmaK<TL>::HALO_INS % GeoDmaK<TL>::NW == 0, "whole DMA instructions per wave");
+    __shared__ __attribute__((aligned(16))) unsigned char
+        smem[DMA == 1 ? GeoDma<TL>::LDS : DMA == 2 ? GeoDmaK<TL>::LDS : TL::LDS];
     unsigned char* halo = smem;
     unsigned char* wl = smem + TL::HPOS * kGRow;
 
@@ -388,7 +419,7 @@ __global__ __launch_bounds__(TL::NT) __attribute__((amdgpu_waves_per_eu(TL::OCC)
         }
     };
 
-    if constexpr (DMA) {
+    if constexpr (DMA == 1) {
         typedef __attribute__((address_space(3))) void lds_t;
         using DL = GeoDma<TL>;
         constexpr int NW = DL::NW;
@@ -458,6 +489,107 @@ __global__ __launch_bounds__(TL::NT) __attribute__((amdgpu_waves_per_eu(TL::OCC)
             asm volatile("" ::: "memory");
             if (ch + 1 < nChunk) stage(ch + 1, smem + ((ch + 1) & 1) * DL::BUF);
             compute(smem + (ch & 1) * DL::BUF);
+        }
+    } else if constexpr (DMA == 2) {
+        typedef __attribute__((address_space(3))) void lds_t;
+        using DL = GeoDmaK<TL>;
+        constexpr int NW = DL::NW;
+        constexpr int CK = Elem<false>::CK;
+        const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+        unsigned char* const wbuf = smem + DL::HALO_BYTES;
+        // Staged columns start at the 4-pixel run holding input column ow0 - P; the tile's
+        // column j, tap kw reads staged column j + kw + mis.
+        const int mis = ((-pad) % 4 + 4) % 4;
+        const int ih0 = oh0 - pad, iwa = ow0 - pad - mis;
+        // Lane l: halo row (row group) * 6 + l / 10, run l % 10. A run lies wholly inside or
+        // outside the image (W % 4 == 0); rows and runs outside it, and channels past Cin, read zero.
+        const int lr = lane / 10, lrun = lane - 10 * (lane / 10);
+        const int lane_off = (lr * W + 4 * lrun) * 4;
+        const bool lane_ok = lr < DL::RG && iwa + 4 * lrun >= 0 && iwa + 4 * lrun < W;
+        const bool row_ok0 = lane_ok && lr < DL::HR && ih0 + lr >= 0 && ih0 + lr < H;
+        const bool row_ok1 = lane_ok && DL::RG + lr < DL::HR && ih0 + DL::RG + lr >= 0 && ih0 + DL::RG + lr < H;
+        const int w_lane = ((lane >> 2) * 4 + ((lane & 3) ^ ((lane >> 3) & 3))) * 16;
+        auto stage_halo = [&](int ch) {
+            const int c0 = ch * CK;
+#pragma unroll
+            for (int k = 0; k < DL::HALO_INS / NW; ++k) {
+                const int ins = wave_u + NW * k;
+                const int c = ins >> 1, rg = ins & 1;  // wave-uniform
+                // unsigned, so that a channel past Cin (kOOB below) or a base row or column
+                // before the image wraps instead of overflowing; in-image lanes get the
+                // exact offset back
+                const int ubase = (int)__builtin_amdgcn_readfirstlane(
+                    (((unsigned)(c0 + c) * H + (unsigned)(ih0 + rg * DL::RG)) * W + (unsigned)iwa) * 4u);
+                const bool in = c0 + c < Cin && (rg ? row_ok1 : row_ok0);
+                const int off = in ? ubase + lane_off : kOOB;
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    xr, (lds_t*)(smem + c * 2048 + ((c >> 2) & 3) * 64 + rg * 1024), 16, off, 0, 0, 0);
+            }
+        };
+        // Weights of kernel row kh: instruction ins fills rows 16 ins .. 16 ins + 15 of [kw][BN]
+        // (tap and first oc wave-uniform, BN a multiple of 16); lane l takes row 16 ins + l / 4
+        // and 16-byte slot l % 4, which holds K group (l % 4) ^ ((l / 4 >> 1) & 3).
+        auto stage_w = [&](int ch, int kh, unsigned char* wb) {
+#pragma unroll
+            for (int k = 0; k < DL::W_INS / NW; ++k) {
+                const int ins = wave_u + NW * k;
+                const int kw = (ins * 16) / TL::BN, o0 = (ins * 16) % TL::BN;
+                const int ubase =
+                    __builtin_amdgcn_readfirstlane((((ch * KS + kh) * KS + kw) * CoutPad + oc0 + o0) * 64);
+                const int off = ins * 16 < DL::W_ROWS ? ubase + w_lane : kOOB;
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, (lds_t*)(wb + ins * 1024), 16, off, 0, 0, 0);
+            }
+        };
+        // The K taps of kernel row kh, in the register path's order (kw, channel group, pixel
+        // block, oc block), so both paths round identically.
+        auto compute_kh = [&](int kh, const unsigned char* wb) {
+#pragma unroll
+            for (int kw = 0; kw < KS; ++kw) {
+                u4 b[TL::WOB];
+#pragma unroll
+                for (int j = 0; j < TL::WOB; ++j) {
+                    const int o = (woi * TL::WOB + j) * 16 + i;
+                    b[j] = *(const u4*)(wb + (kw * TL::BN + o) * 64 + 16 * (g ^ ((i >> 1) & 3)));
+                }
+                unsigned a[TL::WPB][4];
+#pragma unroll
+                for (int j = 0; j < TL::WPB; ++j) {
+                    const int pb = wpi * TL::WPB + j;
+                    const unsigned char* q = smem + g * (4 * 2048 + 64) + DL::row_off(pb_row(pb) + kh) +
+                                             (pb_col(pb) * 16 + i + kw + mis) * 4;
+#pragma unroll
+                    for (int s4 = 0; s4 < 4; ++s4) a[j][s4] = *(const unsigned*)(q + s4 * 2048);
+                }
+#pragma unroll
+                for (int s4 = 0; s4 < 4; ++s4)
+#pragma unroll
+                    for (int jp = 0; jp < TL::WPB; ++jp)
+#pragma unroll
+                        for (int jo = 0; jo < TL::WOB; ++jo)
+                            acc[jp][jo] = __builtin_amdgcn_mfma_f32_16x16x4f32(
+                                __uint_as_float(a[jp][s4]), __uint_as_float(b[jo][s4]), acc[jp][jo], 0, 0, 0);
+            }
+        };
+        for (int ch = 0; ch < nChunk; ++ch) {
+            if (ch) {  // every wave is done reading the previous chunk's halo and weights
+                asm volatile("" ::: "memory");
+                __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+                __builtin_amdgcn_s_barrier();
+                asm volatile("" ::: "memory");
+            }
+            stage_halo(ch);
+            stage_w(ch, 0, wbuf);
+#pragma unroll
+            for (int kh = 0; kh < KS; ++kh) {
+                // the halo and row kh's weights have landed (this wave's, then every wave's),
+                // and no wave still reads the other weight buffer (row kh - 1)
+                asm volatile("" ::: "memory");
+                __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0)
+                __builtin_amdgcn_s_barrier();
+                asm volatile("" ::: "memory");
+                if (kh + 1 < KS) stage_w(ch, kh + 1, wbuf + ((kh + 1) & 1) * DL::WBUF);
+                compute_kh(kh, wbuf + (kh & 1) * DL::WBUF);
+            }
         }
     } else {
         // Steps (chunk c, kernel row kh), kh fastest; the next step's loads fly while this
@@ -610,9 +742,9 @@ __global__ __launch_bounds__(TL::NT) __attribute__((amdgpu_waves_per_eu(TL::OCC)
     }
 }
 
-// DMA: the caller has checked that the layer has 16-byte halo runs (W % 4 == 0, x 16-byte
-// aligned) and no padding.
-template <bool BF16, int ACT, bool POOL, class TL, bool DMA = false>
+// DMA (1 or 2): the caller has checked that the layer is fp32 with 16-byte halo runs (W % 4 ==
+// 0, x 16-byte aligned), stride 1, and for the 1x1 form no padding.
+template <bool BF16, int ACT, bool POOL, class TL, int DMA = 0>
 hipError_t launch_geo_typed(const ConvPlan& p, const void* x, const void* wpk, const float* b, float* dst,
                             hipStream_t stream) {
     using T = typename Elem<BF16>::T;
@@ -622,8 +754,8 @@ hipError_t launch_geo_typed(const ConvPlan& p, const void* x, const void* wpk, c
     constexpr bool kVecOK = !(BF16 && TL::KS == 5 && TL::S == 2);
     const bool vec = kVecOK && p.W % (16 / (int)sizeof(T)) == 0 && (uintptr_t)x % 16 == 0;
     auto kern = conv_general_fused<BF16, false, ACT, POOL, TL>;
-    if constexpr (DMA)
-        kern = conv_general_fused<false, true, ACT, POOL, TL, true>;
+    if constexpr (DMA != 0)
+        kern = conv_general_fused<false, true, ACT, POOL, TL, DMA>;
     else if constexpr (kVecOK)
         if (vec) kern = conv_general_fused<BF16, true, ACT, POOL, TL>;
     hipLaunchKernelGGL(kern, dim3((unsigned)p.grid()), dim3(TL::NT), 0, stream,
@@ -633,7 +765,7 @@ hipError_t launch_geo_typed(const ConvPlan& p, const void* x, const void* wpk, c
     return hipGetLastError();
 }
 
-template <bool BF16, class TL, bool DMA = false>
+template <bool BF16, class TL, int DMA = 0>
 hipError_t launch_geo_act(const ConvPlan& p, const void* x, const void* wpk, const float* b, float* dst,
                           hipStream_t stream) {
     switch (p.act * 2 + p.pool) {

@@ -167,6 +167,42 @@ def test_conv2d_1x1_f32_dma_matches_register_path(shape):
         assert torch.equal(o_dma, o_reg), (act, pool)
 
 
+# fp32 stride-1 layers with K = 3 or 5 and W % 4 == 0 stage by LDS DMA as well (a 16-byte
+# aligned x); the same layer with x 4 bytes past a 16-byte boundary takes the register path.
+# Both accumulate in the same order, so the outputs agree bit for bit: every padding below K
+# (the staged window's offset from a 4-pixel run differs for each), 16-, 32- and 64-channel
+# tiles, a 65-channel layer (two oc tiles), channel tails and several chunks.
+DMA_KXK = [
+    (3, 1, (2, 5, 13, 20, 7)),
+    (3, 2, (1, 17, 11, 36, 33)),
+    (5, 2, (2, 16, 19, 28, 64)),
+    (5, 1, (1, 40, 9, 44, 65)),
+    (5, 3, (1, 3, 21, 24, 16)),
+    (5, 4, (2, 33, 8, 12, 20)),
+    (5, 0, (1, 64, 30, 40, 64)),
+]
+
+
+@pytest.mark.parametrize("K,P,shape", DMA_KXK)
+def test_conv2d_kxk_f32_dma_matches_register_path(K, P, shape):
+    x, w, b = rand_case(K * 10 + P + hash(shape) % 953, *shape, K)
+    xd = to_device(x)
+    flat = torch.empty(xd.numel() + 1, dtype=torch.float32, device=xd.device)
+    flat[1:] = xd.reshape(-1)
+    xu = flat[1:].view(xd.shape)
+    assert xd.data_ptr() % 16 == 0 and xu.data_ptr() % 16 != 0
+    wd, bd = to_device(w), to_device(b)
+    for act, pool in (("gelu", True), ("mish2", False)):
+        o_dma = fc.conv2d_act_pool(xd, wd, bd, stride=1, pad=P, act=act, pool=pool)
+        o_reg = fc.conv2d_act_pool(xu, wd, bd, stride=1, pad=P, act=act, pool=pool)
+        torch.cuda.synchronize()
+        assert torch.equal(o_dma, o_reg), (act, pool)
+    got = o_dma.cpu().numpy()
+    err = max_rel_err(got, oracle.conv2d_act_pool(x, w, b, 1, P, fc.ACT_MISH2, 0))
+    print(f"K={K} P={P} shape={shape} err={err:.3e}", flush=True)
+    assert err <= TOL_F32
+
+
 def _random_case(rng):
     K = int(rng.choice([1, 3, 5]))
     S = int(rng.choice([1, 2]))
