@@ -26,8 +26,8 @@
 // output columns of a fragment read 16 consecutive LDS rows for every tap -- the same
 // conflict-free pattern as stride 1.
 //
-// fp32 1x1 stride-1 layers of 128 or more output channels with 16-byte halo runs stage
-// each chunk by LDS DMA into a double buffer instead (GeoDma below), and fp32 stride-1 3x3
+// fp32 1x1 stride-1 layers with 16-byte halo runs stage each chunk by LDS DMA into a double
+// buffer instead (GeoDma below), and fp32 stride-1 3x3
 // and 5x5 layers with 16-byte halo runs stage each chunk's whole halo, and each kernel row's
 // weights, by LDS DMA (GeoDmaK below).
 //

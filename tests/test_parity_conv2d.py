@@ -145,13 +145,14 @@ def test_conv2d_narrow_layer_tile_full_size_whole_output():
     assert err <= TOL_F32
 
 
-# fp32 1x1 stride-1 layers of 128 or more output channels with W % 4 == 0 and a 16-byte aligned
-# x stage by LDS DMA; an x 4 bytes past a 16-byte boundary takes the element-wise register
-# path. Both accumulate chunk by chunk and channel group by channel group from the bias, so
-# the outputs agree bit for bit: ragged rows and columns, a 1-channel second oc tile, a
-# channel tail chunk, and a larger image.
+# fp32 1x1 stride-1 layers with W % 4 == 0 and a 16-byte aligned x stage by LDS DMA; an x 4
+# bytes past a 16-byte boundary takes the element-wise register path. Both accumulate chunk by
+# chunk and channel group by channel group from the bias, so the outputs agree bit for bit:
+# ragged rows and columns, a 1-channel second oc tile, a channel tail chunk, a larger image,
+# and the 16-, 32- and 64-channel tiles of narrower layers.
 @pytest.mark.parametrize("shape", [(1, 64, 17, 48, 144), (2, 8, 11, 24, 129), (3, 40, 21, 36, 200),
-                                   (8, 64, 64, 64, 128)])
+                                   (8, 64, 64, 64, 128), (1, 16, 11, 36, 7), (2, 40, 13, 28, 20),
+                                   (3, 64, 9, 44, 64), (1, 33, 10, 16, 65)])
 def test_conv2d_1x1_f32_dma_matches_register_path(shape):
     x, w, b = rand_case(hash(shape) % 967 + 9, *shape, 1)
     xd = to_device(x)
