@@ -181,6 +181,8 @@ DMA_KXK = [
     (5, 3, (1, 3, 21, 24, 16)),
     (5, 4, (2, 33, 8, 12, 20)),
     (5, 0, (1, 64, 30, 40, 64)),
+    (5, 4, (1, 3, 1, 4, 5)),       # one input row, one 4-pixel run: padding on every side
+    (3, 2, (2, 1, 2, 4, 3)),       # one input channel, a 2 x 4 image
 ]
 
 
