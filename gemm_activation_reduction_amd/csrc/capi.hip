@@ -202,7 +202,10 @@ int conv_impl(const char* name, const void* x, const void* w, const float* b, in
     if (!known_act(kind)) return fail(FCONV_EINVAL, fn + ": unknown activation " + std::to_string(kind));
     if (dt != FCONV_DT_F32 && dt != FCONV_DT_BF16) return fail(FCONV_EINVAL, fn + ": unknown dtype bits in act");
     if (pool != 0 && pool != 1) return fail(FCONV_EINVAL, fn + ": pool must be 0 or 1");
-    const bool fast = K == 3 && stride == 1 && pad == 0;
+    const bool bf16_in = (act & ~0xFF) == FCONV_DT_BF16;
+    // 3x3 stride 1: valid layers, and bf16 "same" layers (pad 1) of 256 or more output channels
+    // with 16-byte halo runs, take the 3x3 kernels
+    const bool fast = K == 3 && stride == 1 && (pad == 0 || (pad == 1 && fconv::conv3x3_same_wide(bf16_in, W, Cout, x)));
     if (!fast && !fconv::conv_general_supported(K, stride))
         return fail(FCONV_EUNSUPPORTED, fn + ": kernel size must be 1, 3 or 5 and stride 1 or 2");
     if (pad >= K) return fail(FCONV_EUNSUPPORTED, fn + ": padding must be smaller than the kernel size");
@@ -217,7 +220,7 @@ int conv_impl(const char* name, const void* x, const void* w, const float* b, in
         return fail(FCONV_EINVAL, fn + ": out overlaps an input");
 
     const bool bf16 = dt == FCONV_DT_BF16;
-    const fconv::ConvPlan plan = fast ? fconv::plan_conv(bf16, kind, pool, N, Cin, H, W, Cout, x)
+    const fconv::ConvPlan plan = fast ? fconv::plan_conv(bf16, kind, pool, N, Cin, H, W, Cout, x, pad)
                                       : fconv::plan_conv_general(bf16, kind, pool, N, Cin, H, W, Cout, K, stride, pad);
     if (plan.grid() > 0x7FFFFFFFLL) return fail(FCONV_EUNSUPPORTED, fn + ": launch grid too large");
     // The kernels address one image of x, and the repacked weights, with 32-bit byte offsets.

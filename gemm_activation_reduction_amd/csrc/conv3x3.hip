@@ -631,9 +631,13 @@ constexpr int kWHP = 40;                                    // halo positions pe
 constexpr int kWideHalo = TileW::HR * kWHP * 64;            // 6 rows x 40 positions x 64 bytes
 constexpr int kWideLds = kWideSlots * kWideSlot + kWideHalo + kRawA + kRawB;
 static_assert(TileW::HR == 6 && TileW::HC == 34 && Elem<true>::CK == 32, "raw halo staging covers 32 x 6 x 34");
-static_assert(2 * kWideLds <= 160 * 1024, "two wide workgroups per CU");
+static_assert(2 * (kWideLds + 1024) <= 160 * 1024, "two wide workgroups per CU");
 
-template <int ACT, bool POOL>
+// PAD = 1 is the zero-padded ("same") 3x3 layer: the halo starts one row and one column
+// before the tile, so halo column 0 comes from a third set of 4-byte runs (input columns
+// ow0 - 2, ow0 - 1), the 16-byte runs land one position to the right, and halo column 33
+// is the first pixel of the 4-byte run at ow0 + 32. Rows and columns outside x read zero.
+template <int ACT, bool POOL, int PAD = 0>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void conv3x3_wide_bf16(
     const unsigned short* __restrict__ x, const unsigned short* __restrict__ wp, const float* __restrict__ bias,
     float* __restrict__ dst, int Cin, int H, int W, int Cout, int CoutPad, int nChunk, int tilesH, int tilesW,
@@ -641,7 +645,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void c
     using TL = TileW;
     constexpr int CK = Elem<true>::CK;
     static_assert(TL::NT == 256 && TL::WPB == 4 && TL::WOB == 8 && TL::CB == 2, "wide tile shape");
-    __shared__ __attribute__((aligned(1024))) unsigned char smem[kWideLds];
+    static_assert(PAD == 0 || PAD == 1, "valid or one-pixel zero padding");
+    __shared__ __attribute__((aligned(1024))) unsigned char smem[kWideLds + PAD * 1024];
     unsigned char* ring = smem;
     unsigned char* halo = smem + kWideSlots * kWideSlot;
     unsigned char* raw = halo + kWideHalo;
@@ -651,7 +656,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void c
     const int tw = bid % tilesW; bid /= tilesW;
     const int th = bid % tilesH;
     const int n = bid / tilesH;
-    const int OH = H - 2, OW = W - 2;
+    const int OH = H - 2 + 2 * PAD, OW = W - 2 + 2 * PAD;
     const int oh0 = th * TL::TH, ow0 = tw * TL::TW, oc0 = ot * TL::BN;
 
     const int tid = threadIdx.x, lane = tid & 63;
@@ -713,19 +718,40 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void c
             const int ei = ia * 64 + lane;
             const int e = ei / 96, rem = ei % 96;
             const int q = rem & 3, cg = (rem >> 2) & 3, r = rem >> 4;
-            const int ch = c0 + 8 * q + e, ih = oh0 + r, iw = ow0 + 8 * cg;
-            const int off = (ch < Cin && ih < H && iw < W) ? ((ch * H + ih) * W + iw) * 2 : kOOB;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (lds_t*)(raw + ia * 1024), 16, off, 0, 0, 0);
+            if constexpr (PAD == 0) {
+                const int ch = c0 + 8 * q + e, ih = oh0 + r, iw = ow0 + 8 * cg;
+                const int off = (ch < Cin && ih < H && iw < W) ? ((ch * H + ih) * W + iw) * 2 : kOOB;
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (lds_t*)(raw + ia * 1024), 16, off, 0, 0, 0);
+            } else {
+                const int ch = c0 + 8 * q + e, ih = oh0 - 1 + r, iw = ow0 + 8 * cg;
+                const int off = (ch < Cin && (unsigned)ih < (unsigned)H && iw < W) ? ((ch * H + ih) * W + iw) * 2 : kOOB;
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (lds_t*)(raw + ia * 1024), 16, off, 0, 0, 0);
+            }
         }
-        {
+        if constexpr (PAD == 0) {
             const int ei = wave * 64 + lane;  // 192 entries; lanes 192-255 pad
             const int e = ei / 24, rem = ei % 24;
             const int q = rem & 3, r = rem >> 2;
             const int ch = c0 + 8 * q + e, ih = oh0 + r, iw = ow0 + 32;
             const int off = (ei < 192 && ch < Cin && ih < H && iw < W) ? ((ch * H + ih) * W + iw) * 2 : kOOB;
             __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (lds_t*)(raw + kRawA + wave * 256), 4, off, 0, 0, 0);
+        } else {
+            // the right 4-byte runs (ow0 + 32) and the left ones (ow0 - 2) of one entry share
+            // its channel and row: one base, 68 bytes apart
+            const int ei = wave * 64 + lane;  // 192 entries; lanes 192-255 pad
+            const int e = ei / 24, rem = ei % 24;
+            const int q = rem & 3, r = rem >> 2;
+            const int ch = c0 + 8 * q + e, ih = oh0 - 1 + r;
+            const bool in = ei < 192 && ch < Cin && (unsigned)ih < (unsigned)H;
+            // unsigned: a channel past Cin or a row before x (both kOOB below) wraps harmlessly
+            const int base = (int)(((unsigned)(ch * H + ih) * (unsigned)W + (unsigned)(ow0 + 32)) * 2u);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (lds_t*)(raw + kRawA + wave * 256), 4,
+                                                     in && ow0 + 32 < W ? base : kOOB, 0, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (lds_t*)(raw + kRawA + 1024 + wave * 256), 4,
+                                                     in && ow0 > 0 ? base - 68 : kOOB, 0, 0, 0);
         }
     };
+    constexpr int kHaloDma = 4 + PAD;  // halo DMA instructions per wave
     // Raw staging -> channel-minor halo positions (the layout the A fragments read): item
     // (channel group q, column group cg, halo row r) gathers its 8 channels' runs and writes
     // pixel p of them as one 16-byte group (a byte permute per output dword) to halo position
@@ -739,9 +765,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void c
 #pragma unroll
                 for (int e = 0; e < 8; ++e) v[e] = *(const u4*)(raw + (e * 96 + (r * 4 + cg) * 4 + q) * 16);
             } else {
+                // PAD: dword 1 holds the left run (its pixel 1 is halo column 0)
 #pragma unroll
                 for (int e = 0; e < 8; ++e)
-                    v[e] = u4{*(const unsigned*)(raw + kRawA + (e * 24 + r * 4 + q) * 4), 0u, 0u, 0u};
+                    v[e] = u4{*(const unsigned*)(raw + kRawA + (e * 24 + r * 4 + q) * 4),
+                              PAD ? *(const unsigned*)(raw + kRawA + 1024 + (e * 24 + r * 4 + q) * 4) : 0u, 0u, 0u};
             }
 #pragma unroll
             for (int p = 0; p < 8; ++p) {
@@ -750,7 +778,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void c
                 u4 o;
 #pragma unroll
                 for (int k = 0; k < 4; ++k) o[k] = __builtin_amdgcn_perm(v[2 * k + 1][dw], v[2 * k][dw], sel);
-                const int pos = r * kWHP + cg * 8 + p;
+                // PAD, 4-byte item: pixel 0 is halo column 33 and pixel 3 (the left run's second
+                // pixel) column 0; the other six land in columns 34-39, which no fragment reads
+                constexpr int kEdge[8] = {33, 34, 35, 0, 37, 38, 39, 36};
+                const int col = (PAD && cg == 4) ? kEdge[p] : cg * 8 + p + PAD;
+                const int pos = r * kWHP + col;
                 *(u4*)(halo + pos * 64 + 16 * (q ^ ((pos >> 1) & 3))) = o;
             }
         }
@@ -803,11 +835,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void c
             // Before the barrier: this wave's reads of this step are done (the next step's DMA
             // reuses the slot read here) and its DMA of step s + 1 has landed. Vector memory
             // operations complete in order; the DMA instructions sent after step s + 1's may stay
-            // in flight: step s + 2's (4) and, in taps 0 and 1, the next chunk's halo (4). The
-            // halo has landed by the end of tap 2, long before its transpose after tap 8.
-            const int after = (ahead ? 4 : 0) + ((NEXT && t <= 1) ? 4 : 0);
+            // in flight: step s + 2's (4) and, in taps 0 and 1, the next chunk's halo (kHaloDma).
+            // The halo has landed by the end of tap 2, long before its transpose after tap 8.
+            const int after = (ahead ? 4 : 0) + ((NEXT && t <= 1) ? kHaloDma : 0);
             asm volatile("" ::: "memory");
-            if (after == 8) __builtin_amdgcn_s_waitcnt(0x0078);       // vmcnt(8) lgkmcnt(0)
+            if (after == 9) __builtin_amdgcn_s_waitcnt(0x0079);       // vmcnt(9) lgkmcnt(0)
+            else if (after == 8) __builtin_amdgcn_s_waitcnt(0x0078);  // vmcnt(8) lgkmcnt(0)
+            else if (after == 5) __builtin_amdgcn_s_waitcnt(0x0075);  // vmcnt(5) lgkmcnt(0)
             else if (after == 4) __builtin_amdgcn_s_waitcnt(0x0074);  // vmcnt(4) lgkmcnt(0)
             else __builtin_amdgcn_s_waitcnt(0x0070);                  // vmcnt(0) lgkmcnt(0)
             __builtin_amdgcn_s_barrier();
@@ -939,7 +973,8 @@ hipError_t launch_act(const ConvPlan& p, const void* x, const void* wpk, const f
 template <int ACT, bool POOL>
 hipError_t launch_wide_typed(const ConvPlan& p, const void* x, const void* wpk, const float* b, float* dst,
                              hipStream_t stream) {
-    hipLaunchKernelGGL((conv3x3_wide_bf16<ACT, POOL>), dim3((unsigned)p.grid()), dim3(TileW::NT), 0, stream,
+    auto kern = p.pad ? conv3x3_wide_bf16<ACT, POOL, 1> : conv3x3_wide_bf16<ACT, POOL, 0>;
+    hipLaunchKernelGGL(kern, dim3((unsigned)p.grid()), dim3(TileW::NT), 0, stream,
                        (const unsigned short*)x, (const unsigned short*)wpk, b, dst, p.Cin, p.H, p.W, p.Cout,
                        p.CoutPad, p.nChunk, p.tilesH, p.tilesW, p.ocTiles,
                        ((uintptr_t)dst % 16 == 0) ? 16 : ((uintptr_t)dst % 8 == 0 ? 8 : 4));
@@ -963,12 +998,16 @@ hipError_t launch_wide(const ConvPlan& p, const void* x, const void* wpk, const 
 
 }  // namespace
 
-ConvPlan plan_conv(bool bf16, int act, int pool, int N, int Cin, int H, int W, int Cout, const void* x) {
+bool conv3x3_same_wide(bool bf16, int W, int Cout, const void* x) {
+    return bf16 && W % 8 == 0 && (uintptr_t)x % 16 == 0 && Cout >= TileW::BN;
+}
+
+ConvPlan plan_conv(bool bf16, int act, int pool, int N, int Cin, int H, int W, int Cout, const void* x, int pad) {
     ConvPlan p{};
     p.bf16 = bf16; p.act = act; p.pool = pool;
     p.N = N; p.Cin = Cin; p.H = H; p.W = W; p.Cout = Cout;
-    p.OH = H - 2; p.OW = W - 2;
-    p.KS = 3; p.stride = 1; p.pad = 0; p.general = false;
+    p.OH = H - 2 + 2 * pad; p.OW = W - 2 + 2 * pad;
+    p.KS = 3; p.stride = 1; p.pad = pad; p.general = false;
     // bf16 with 256 or more output channels and 16-byte halo loads: the wide kernel
     const bool vec = W % 8 == 0 && (uintptr_t)x % 16 == 0;
     p.wide = bf16 && vec && Cout >= TileW::BN;
@@ -990,6 +1029,7 @@ ConvPlan plan_conv(bool bf16, int act, int pool, int N, int Cin, int H, int W, i
 
 hipError_t launch_conv(const ConvPlan& p, const void* x, const void* w, const float* b, float* out,
                        void* workspace, hipStream_t stream, KernelTimer* timer) {
+    if (p.pad != 0 && !p.wide) return hipErrorInvalidValue;  // only the wide kernel pads
     unsigned char* ws = (unsigned char*)workspace;
     void* wpk = ws;
     float* part = (float*)(ws + p.wpack_bytes);

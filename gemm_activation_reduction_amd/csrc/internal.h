@@ -30,7 +30,9 @@ struct ConvPlan {
     long long grid() const { return (long long)N * tilesH * tilesW * ocTiles; }
 };
 
-ConvPlan plan_conv(bool bf16, int act, int pool, int N, int Cin, int H, int W, int Cout, const void* x);
+// pad 1 (a "same" 3x3 layer) only where conv3x3_same_wide holds: the wide bf16 kernel
+ConvPlan plan_conv(bool bf16, int act, int pool, int N, int Cin, int H, int W, int Cout, const void* x, int pad = 0);
+bool conv3x3_same_wide(bool bf16, int W, int Cout, const void* x);
 hipError_t launch_conv(const ConvPlan& p, const void* x, const void* w, const float* b,
                        float* out, void* workspace, hipStream_t stream, KernelTimer* timer);
 

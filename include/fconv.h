@@ -114,7 +114,9 @@ int fconv_act_pool_noalloc(const void* x, const void* w, const float* b,
  *        out [N][Cout] or [N][Cout][OH][OW].
  *
  * Supported: K in {1, 3, 5}, stride in {1, 2}, 0 <= pad < K. K = 3, stride 1, pad 0 runs
- * the same kernel as fconv_act_pool. Returns FCONV_EINVAL for the fconv_act_pool errors,
+ * the same kernel as fconv_act_pool, and so does a bf16 K = 3, stride 1, pad 1 layer of 256
+ * or more output channels with W % 8 == 0 and a 16-byte aligned x (the wide kernel, padded).
+ * Returns FCONV_EINVAL for the fconv_act_pool errors,
  * K < 1, stride < 1, pad < 0 or a padded input smaller than the kernel;
  * FCONV_EUNSUPPORTED for another K or stride, or pad >= K.
  */

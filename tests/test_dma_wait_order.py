@@ -58,7 +58,7 @@ def counted_region(body):
 
 
 def test_instantiations_found(asm):
-    assert len(asm["conv3x3.hip"]) == 8          # four activations x pooled / full map
+    assert len(asm["conv3x3.hip"]) == 16         # four activations x pooled / full map x valid / padded
     assert len(asm["gemm_lse.hip"]) == 2         # bf16 and fp32 operands
 
 

@@ -206,6 +206,56 @@ def test_conv2d_kxk_f32_dma_matches_register_path(K, P, shape):
     assert err <= TOL_F32
 
 
+# bf16 "same" 3x3 layers (stride 1, pad 1) of 256 or more output channels with W % 8 == 0
+# and a 16-byte aligned x run the wide 3x3 kernel with one pixel of zero padding; an x 2 bytes
+# past a 16-byte boundary takes the general kernel. Both accumulate chunk by chunk and tap by
+# tap from the bias, so full maps agree bit for bit. Pooled outputs sum per-tile partials of
+# different tile shapes (4 or 8 rows), so there both are held to the oracle instead.
+SAME_WIDE = [
+    (1, 40, 14, 48, 300),   # two chunks (an 8-channel tail), two oc tiles
+    (2, 33, 8, 8, 256),     # the narrowest image (one 8-pixel group), a 1-channel tail chunk
+    (1, 64, 9, 32, 257),    # exactly one tile column, a 1-channel second oc tile
+    (1, 3, 5, 40, 256),     # three input channels, a ragged second tile column
+    (3, 96, 13, 24, 256),   # three chunks, three images
+    (1, 32, 1, 16, 256),    # a single input row: padding above and below
+]
+
+
+@pytest.mark.parametrize("shape", SAME_WIDE)
+def test_conv2d_same_bf16_wide_kernel(shape):
+    x, w, b = rand_case(hash(shape) % 941 + 13, *shape, 3, bf16=True)
+    xd = to_device(x, True)
+    flat = torch.empty(xd.numel() + 1, dtype=torch.bfloat16, device=xd.device)
+    flat[1:] = xd.reshape(-1)
+    xu = flat[1:].view(xd.shape)
+    assert xd.data_ptr() % 16 == 0 and xu.data_ptr() % 16 != 0
+    wd, bd = to_device(w, True), to_device(b)
+    for k, pool in enumerate((False, True)):
+        act = ACTS[(k + hash(shape)) % 4]
+        o_wide = fc.conv2d_act_pool(xd, wd, bd, stride=1, pad=1, act=act, pool=pool)
+        o_gen = fc.conv2d_act_pool(xu, wd, bd, stride=1, pad=1, act=act, pool=pool)
+        torch.cuda.synchronize()
+        if not pool:
+            assert torch.equal(o_wide, o_gen), act
+        ref = oracle.conv2d_act_pool(x, w, b, 1, 1, act, int(pool))
+        err = max_rel_err(o_wide.cpu().numpy(), ref)
+        err_gen = max_rel_err(o_gen.cpu().numpy(), ref)
+        print(f"same wide shape={shape} act={act} pool={pool} err={err:.3e} (general {err_gen:.3e})", flush=True)
+        # bf16 products are exact in fp32 and accumulate in fp32: the fp32 bound applies
+        assert err <= TOL_F32 and err_gen <= TOL_F32
+
+
+def test_conv2d_same_bf16_wide_full_size_pooled():
+    # the 16 x 128 x 128^2 -> 256 layer with "same" padding: every pooled output
+    x, w, b = rand_case(77, 16, 128, 128, 128, 256, 3, bf16=True)
+    print("same wide full size: running GPU", flush=True)
+    got = run_conv2d(x, w, b, 1, 1, fc.ACT_GELU, 1, True)
+    assert got.shape == (16, 256) and np.all(np.isfinite(got))
+    err = max_rel_err(got, oracle.conv2d_act_pool(x, w, b, 1, 1, fc.ACT_GELU, 1))
+    print(f"same wide full size: all {got.size} outputs, err={err:.3e}", flush=True)
+    assert err <= TOL_F32
+
+
 def _random_case(rng):
     K = int(rng.choice([1, 3, 5]))
     S = int(rng.choice([1, 2]))
