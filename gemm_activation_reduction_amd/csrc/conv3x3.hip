@@ -12,7 +12,9 @@
 // without atomics.
 //
 // bf16 with 256 or more output channels (and 16-byte halo loads) runs conv3x3_wide_bf16
-// instead: 256 oc per workgroup, weights streamed per tap into LDS by DMA (see there).
+// instead: 256 oc per workgroup, weights streamed per tap into LDS by DMA (see there); its
+// PAD = 1 instantiation serves bf16 "same" 3x3 layers as well. fp32 layers with 16-byte halo
+// runs stage each chunk by LDS DMA in NCHW order (DmaLayout) instead of through registers.
 //
 // The operation is the Conv2d -> activation (-> AdaptiveAvgPool2d(1)) chain of
 // the "Kimi-K2.6 l2_p67" and "Kimi-K2.6 l2_p4" POPCORNBENCH pages; the pages'
