@@ -398,9 +398,10 @@ def prepare(name, torch, fc, dev):
 
         def step():
             fc.conv2d_act_pool(xd, wd, bd, stride=S, pad=P, act=act, pool=bool(spec["pool"]), out=out)
-        # the 3x3 path runs the wide kernel for bf16 with Cout >= 256 (the library's timer
-        # names whichever ran)
-        kernels = ["conv3x3_fused", "conv3x3_wide_bf16"] if (K, S, P) == (3, 1, 0) else ["conv_general_fused"]
+        # the 3x3 path runs the wide kernel for bf16 with Cout >= 256, also with pad 1 (the
+        # library's timer names whichever ran)
+        kernels = (["conv3x3_fused", "conv3x3_wide_bf16"] if (K, S, P) == (3, 1, 0) else
+                   ["conv3x3_wide_bf16", "conv_general_fused"] if (K, S, P) == (3, 1, 1) else ["conv_general_fused"])
         w_.update(host=(x, w, b), step=step, out=out, flops=conv_flops(spec), nbytes=conv_bytes(spec),
                   kernels=kernels, dtype=spec["dtype"],
                   cfg={"workload": name, "x": [spec["N"], spec["Cin"], spec["H"], spec["W"]], "cout": spec["Cout"],

@@ -124,6 +124,10 @@ CONV_WORKLOADS = {
     "conv1x1_mish2_full_f32": dict(cfg=11, N=32, Cin=64, H=192, W=192, Cout=128, K=1, stride=1, pad=0,
                                    act=ACT_MISH2, pool=0, dtype="f32", x_dist=("normal",),
                                    w_bound=1.0 / math.sqrt(64), b_bound=0.1),
+    # the bf16 3x3 layer of the pages' shape with "same" zero padding (output 128 x 128)
+    "conv3x3_same_gelu_pool_bf16": dict(cfg=12, N=16, Cin=128, H=128, W=128, Cout=256, K=3, stride=1, pad=1,
+                                        act=ACT_GELU, pool=1, dtype="bf16", x_dist=("normal",),
+                                        w_bound=1.0 / math.sqrt(128 * 9), b_bound=0.1),
     # the same bf16 inputs (same seeds) with the tanh-approximation GELU epilogue
     "conv_gelu_tanh_pool_bf16": dict(cfg=4, N=16, Cin=128, H=128, W=128, Cout=256, act=ACT_GELU_TANH, pool=1,
                                      dtype="bf16", x_dist=("normal",), w_bound=1.0 / math.sqrt(128 * 9),

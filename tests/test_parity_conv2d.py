@@ -246,8 +246,9 @@ def test_conv2d_same_bf16_wide_kernel(shape):
 
 
 def test_conv2d_same_bf16_wide_full_size_pooled():
-    # the 16 x 128 x 128^2 -> 256 layer with "same" padding: every pooled output
-    x, w, b = rand_case(77, 16, 128, 128, 128, 256, 3, bf16=True)
+    # the 16 x 128 x 128^2 -> 256 layer with "same" padding (the bench workload's inputs):
+    # every pooled output
+    x, w, b = workload_conv_inputs("conv3x3_same_gelu_pool_bf16")
     print("same wide full size: running GPU", flush=True)
     got = run_conv2d(x, w, b, 1, 1, fc.ACT_GELU, 1, True)
     assert got.shape == (16, 256) and np.all(np.isfinite(got))
