@@ -314,9 +314,16 @@ def test_conv_wide_matches_narrow_full_map(shape):
     xu = flat[1:].view(xd.shape)
     assert xd.data_ptr() % 16 == 0 and xu.data_ptr() % 16 != 0
     wd, bd = to_device(w, True), to_device(b)
+    fc.fconv_profile(True)
     o_wide = fc.conv_act_pool(xd, wd, bd, act="mish2", pool=False)
+    torch.cuda.synchronize()
+    ran_wide = fc.fconv_profile_read("conv3x3_wide_bf16")[1]
+    fc.fconv_profile(True)
     o_narrow = fc.conv_act_pool(xu, wd, bd, act="mish2", pool=False)
     torch.cuda.synchronize()
+    ran_narrow = fc.fconv_profile_read("conv3x3_fused")[1]
+    fc.fconv_profile(False)
+    assert ran_wide == 1 and ran_narrow == 1, (ran_wide, ran_narrow)  # each call ran the kernel named
     assert torch.equal(o_wide, o_narrow)
 
 

@@ -232,9 +232,17 @@ def test_conv2d_same_bf16_wide_kernel(shape):
     wd, bd = to_device(w, True), to_device(b)
     for k, pool in enumerate((False, True)):
         act = ACTS[(k + hash(shape)) % 4]
+        # the library's per-kernel timers name the kernel each call ran
+        fc.fconv_profile(True)
         o_wide = fc.conv2d_act_pool(xd, wd, bd, stride=1, pad=1, act=act, pool=pool)
+        torch.cuda.synchronize()
+        ran_wide = fc.fconv_profile_read("conv3x3_wide_bf16")[1]
+        fc.fconv_profile(True)
         o_gen = fc.conv2d_act_pool(xu, wd, bd, stride=1, pad=1, act=act, pool=pool)
         torch.cuda.synchronize()
+        ran_gen = fc.fconv_profile_read("conv_general_fused")[1]
+        fc.fconv_profile(False)
+        assert ran_wide == 1 and ran_gen == 1, (ran_wide, ran_gen)
         if not pool:
             assert torch.equal(o_wide, o_gen), act
         ref = oracle.conv2d_act_pool(x, w, b, 1, 1, act, int(pool))
