@@ -305,8 +305,9 @@ struct GeoDma {
 // 0-5 in its first kilobyte and rows 6-11 in its second (160 bytes each), one DMA instruction
 // per (channel, 6-row group) with lane l taking row l / 10, run l % 10. The weights of one
 // kernel row (K taps x BN rows of 64 bytes, swizzled as above) go into one of two buffers, the
-// next row's DMA flying while this row's K taps compute; all K^2 taps of a 64-channel tile
-// would not leave room for two workgroups per CU.
+// next row's DMA flying while this row's K taps compute. At K = 5 all 25 taps of a 64-channel
+// tile would not leave room for two workgroups per CU; at K = 3 staging all nine with the halo
+// (one barrier per chunk) measured the same as the two row buffers.
 template <class TL>
 struct GeoDmaK {
     static constexpr int NW = TL::NT / 64;
